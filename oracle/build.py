@@ -1,0 +1,29 @@
+"""Builds the CPU oracle (plain C, OpenMP) into ``oracle/liboracle.so``.
+
+Test infrastructure only: the oracle is the checker, never part of the product.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-mf16c",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+           SRC, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
