@@ -1,0 +1,188 @@
+"""MI355X-native sparse-attention indexer hot path.
+
+Thin Python binding over ``libblockscore.so`` (C ABI in ``include/blockscore.h``).
+Every function here only marshals torch tensors into the C call: it checks
+dtypes, devices and contiguity, takes raw device pointers and the current HIP
+stream, and raises if the library returns an error.  All computation runs in
+the HIP kernels; there is no CPU fallback.  If the library is not built this
+module raises on first use.
+
+Steps (same names as the C ABI):
+  idx_score_decode / idx_score_prefill  ->  topk_select_rows  ->  idx_expand_translate
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libblockscore.so")
+
+HEADS = 4
+DIM = 128
+PAGE_TOKENS = 64
+KMAX = 2048
+
+_lib = None
+
+
+class BlockScoreError(RuntimeError):
+    pass
+
+
+def lib():
+    """Loads the HIP library (built by ``block_scoring_top_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise BlockScoreError(
+                f"{LIB_PATH} is missing: build it with `python -m block_scoring_top_amd.build` "
+                "(or __graft_entry__.build()); there is no CPU fallback")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+        score_args = [P, P, i64, P, i32, P, i32, P, i32, i32, i32, P, i64, P, P]
+        for name in ("idx_score_decode", "idx_score_prefill"):
+            f = getattr(L, name)
+            f.argtypes = score_args
+            f.restype = C.c_int
+        L.topk_workspace_bytes.argtypes = [i32, i32, i32]
+        L.topk_workspace_bytes.restype = C.c_size_t
+        L.topk_select_rows.argtypes = [P, i64, P, i32, i32, i32, P, P, P, C.c_size_t, P]
+        L.topk_select_rows.restype = C.c_int
+        L.idx_expand_translate.argtypes = [P, P, i32, P, i32, P, i32, i32, P, i32, P, P, P, i32, P]
+        L.idx_expand_translate.restype = C.c_int
+        L.bs_status_string.argtypes = [C.c_int]
+        L.bs_status_string.restype = C.c_char_p
+        L.bs_abi_version.argtypes = []
+        L.bs_abi_version.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().bs_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise BlockScoreError(f"{what}: {status_string(status)} ({status})")
+
+
+def _ptr(t: Optional[torch.Tensor], dtypes, name: str, device: Optional[torch.device] = None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> C.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return C.c_void_p(s.cuda_stream)
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _score(fn: str, q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores,
+           row_len=None, stream=None):
+    dev = q.device
+    num_rows = int(row_pos.shape[0])
+    num_req = int(req_row_ptr.shape[0]) - 1
+    if q.numel() != num_rows * HEADS * DIM:
+        raise ValueError("q must hold num_rows x 4 x 128 values")
+    if scores.dim() != 2 or scores.shape[0] != num_rows:
+        raise ValueError("scores must be [num_rows, ld]")
+    if row_len is not None and row_len.numel() != num_rows:
+        raise ValueError("row_len must hold num_rows entries")
+    per_page = PAGE_TOKENS // int(c) if int(c) in (1, 4) else 1
+    if kcache.numel() < int(num_pages) * per_page * DIM:
+        raise ValueError("kcache holds fewer than num_pages pages")
+    st = getattr(lib(), fn)(
+        _ptr(q, _BF16, "q", dev), _ptr(kcache, _BF16, "kcache", dev), int(num_pages),
+        _ptr(page_table, _I32, "page_table", dev), int(page_table.shape[1]),
+        _ptr(req_row_ptr, _I32, "req_row_ptr", dev), num_req,
+        _ptr(row_pos, _I32, "row_pos", dev), num_rows, int(c), int(max_vis),
+        _ptr(scores, _F32, "scores", dev), int(scores.stride(0)),
+        _ptr(row_len, _I32, "row_len", dev), _stream(stream, dev))
+    _check(st, fn)
+
+
+def idx_score_decode(q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores,
+                     row_len=None, stream=None):
+    """Paged decode/verify scorer.  See ``idx_score_decode`` in blockscore.h."""
+    _score("idx_score_decode", q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis,
+           scores, row_len, stream)
+
+
+def idx_score_prefill(q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores,
+                      row_len=None, stream=None):
+    """Prefill scorer on the matrix cores.  See ``idx_score_prefill`` in blockscore.h."""
+    _score("idx_score_prefill", q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis,
+           scores, row_len, stream)
+
+
+def topk_workspace_bytes(num_rows: int, max_len: int, k: int) -> int:
+    return int(lib().topk_workspace_bytes(int(num_rows), int(max_len), int(k)))
+
+
+def topk_workspace(num_rows: int, max_len: int, k: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace of the size the call needs (None if none)."""
+    n = topk_workspace_bytes(num_rows, max_len, k)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def topk_select_rows(scores, row_len, max_len, k, sel, sel_count, workspace=None, stream=None):
+    """Exact top-k per FP32 row.  See ``topk_select_rows`` in blockscore.h."""
+    dev = scores.device
+    R = int(scores.shape[0])
+    if sel.dim() != 2 or sel.shape[0] != R or sel.shape[1] != k:
+        raise ValueError("sel must be [num_rows, k]")
+    if sel_count.numel() != R or row_len.numel() != R:
+        raise ValueError("row_len and sel_count must hold num_rows entries")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().topk_select_rows(
+        _ptr(scores, _F32, "scores", dev), int(scores.stride(0)), _ptr(row_len, _I32, "row_len", dev), R,
+        int(max_len), int(k), _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev),
+        _ptr(workspace, (torch.uint8,), "workspace", dev), ws_bytes, _stream(stream, dev))
+    _check(st, "topk_select_rows")
+
+
+def idx_expand_translate(sel, sel_count, k, req_row_ptr, row_pos, c, page_table, out_slots, out_count,
+                         out_pos=None, stream=None):
+    """Expand, append pending, translate.  See ``idx_expand_translate`` in blockscore.h."""
+    dev = sel.device
+    R = int(row_pos.shape[0])
+    if sel.dim() != 2 or sel.shape[0] != R or sel.shape[1] != k:
+        raise ValueError("sel must be [num_rows, k]")
+    if out_slots.dim() != 2 or out_slots.shape[0] != R:
+        raise ValueError("out_slots must be [num_rows, ld_out]")
+    if out_pos is not None and out_pos.shape != out_slots.shape:
+        raise ValueError("out_pos must match out_slots")
+    st = lib().idx_expand_translate(
+        _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev), int(k),
+        _ptr(req_row_ptr, _I32, "req_row_ptr", dev), int(req_row_ptr.shape[0]) - 1,
+        _ptr(row_pos, _I32, "row_pos", dev), R, int(c),
+        _ptr(page_table, _I32, "page_table", dev), int(page_table.shape[1]),
+        _ptr(out_slots, _I32, "out_slots", dev), _ptr(out_pos, _I32, "out_pos", dev),
+        _ptr(out_count, _I32, "out_count", dev), int(out_slots.stride(0)), _stream(stream, dev))
+    _check(st, "idx_expand_translate")
+
+
+__all__ = [
+    "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
+    "topk_select_rows", "idx_expand_translate", "status_string", "BlockScoreError", "lib",
+]

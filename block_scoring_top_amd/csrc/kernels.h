@@ -1,0 +1,37 @@
+// kernels.h - internal launchers behind the C ABI (host side, validated inputs).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bs {
+
+int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_pages,
+                        const int32_t* page_table, int32_t pt_stride,
+                        const int32_t* req_row_ptr, int32_t num_req,
+                        const int32_t* row_pos, int32_t num_rows,
+                        int32_t c, int32_t max_vis,
+                        float* scores, int64_t ld, int32_t* row_len, hipStream_t stream);
+
+int launch_score_prefill(const uint16_t* q, const uint16_t* kcache, int64_t num_pages,
+                         const int32_t* page_table, int32_t pt_stride,
+                         const int32_t* req_row_ptr, int32_t num_req,
+                         const int32_t* row_pos, int32_t num_rows,
+                         int32_t c, int32_t max_vis,
+                         float* scores, int64_t ld, int32_t* row_len, hipStream_t stream);
+
+size_t topk_workspace_size(int32_t num_rows, int32_t max_len, int32_t k);
+
+int launch_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows,
+                int32_t max_len, int32_t k, int32_t* sel, int32_t* sel_count,
+                void* workspace, hipStream_t stream);
+
+int launch_expand(const int32_t* sel, const int32_t* sel_count, int32_t k,
+                  const int32_t* req_row_ptr, int32_t num_req,
+                  const int32_t* row_pos, int32_t num_rows, int32_t c,
+                  const int32_t* page_table, int32_t pt_stride,
+                  int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
+                  int32_t ld_out, hipStream_t stream);
+
+}  // namespace bs

@@ -1,0 +1,168 @@
+// score_decode.hip - paged block scorer for decode and speculative-verify rows.
+//
+// Computes the QSA block score (page "Qwen3.8-Flash-Next Day-0 in SGLang",
+// section on Qwen sparse attention, score equation): for a query row with
+// 4 heads of 128 dims and a compressed key kbar,
+//     s = (1/sqrt(128)) * sum_h max(0, <q_h, kbar>),
+// over the row's visible blocks, reading keys through the page table (the
+// section's paged decode scorer and full_slot/4 addressing).
+//
+// Mapping on gfx950 (64-lane waves, memory bound, no matrix cores):
+//   * a workgroup of 256 lanes owns a chunk of one request's key range and
+//     streams it once, 16 keys (4 KiB) per round, every lane loading one
+//     16-byte slice (8 dims) of one key with a non-temporal load;
+//   * 16 consecutive lanes (one DPP row) hold one key; each lane forms its
+//     partial dot for the 4 heads with v_dot2_f32_bf16 (FP32 accumulate);
+//   * a transposed butterfly over the row (mirror, half-mirror, two quad
+//     swaps) reduces the 4 partial dots in 7 DPP adds, then ReLU per head and
+//     two more DPP adds sum the heads;
+//   * all rows of a request (up to RG at a time) are scored from the same
+//     key registers, so keys leave HBM once per request.
+#include "device.h"
+#include "kernels.h"
+
+namespace bs {
+
+// Sum over the 16 lanes of a DPP row of four per-lane partial dots, ReLU per
+// head, sum over heads.  Every lane of the row returns the unscaled score.
+__device__ __forceinline__ float row_head_relu_sum(float h0, float h1, float h2, float h3, int sub) {
+  const bool hi8 = (sub & 8) != 0;
+  const float keep0 = hi8 ? h2 : h0, keep1 = hi8 ? h3 : h1;
+  const float send0 = hi8 ? h0 : h2, send1 = hi8 ? h1 : h3;
+  const float a0 = keep0 + dpp<kDppRowMirror>(send0);  // partner 15-i: other half
+  const float a1 = keep1 + dpp<kDppRowMirror>(send1);
+  const bool hi4 = (sub & 4) != 0;
+  const float keep = hi4 ? a1 : a0, send = hi4 ? a0 : a1;
+  float x = keep + dpp<kDppRowHalfMirror>(send);  // partner 7-i in the half: bit 2 flipped
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppQuadXor1>(x);
+  // x: full dot of head 2*bit3(sub) + bit2(sub)
+  float y = fmaxf(x, 0.0f);
+  y += dpp<kDppRowHalfMirror>(y);
+  y += dpp<kDppRowMirror>(y);
+  return y;
+}
+
+__device__ __forceinline__ float slice_dot(const u32x4_t& k, const u32x4_t& q) {
+  float acc = 0.0f;
+  acc = dot2_bf16(k.x, q.x, acc);
+  acc = dot2_bf16(k.y, q.y, acc);
+  acc = dot2_bf16(k.z, q.z, acc);
+  acc = dot2_bf16(k.w, q.w, acc);
+  return acc;
+}
+
+template <int RG, int U>
+__global__ __launch_bounds__(256) void score_decode_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kcache, int64_t num_pages,
+    const int32_t* __restrict__ page_table, int32_t pt_stride,
+    const int32_t* __restrict__ req_row_ptr, const int32_t* __restrict__ row_pos,
+    int32_t c, int32_t max_vis, int32_t chunk,
+    float* __restrict__ scores, int64_t ld, int32_t* __restrict__ row_len) {
+  const int b = blockIdx.y;
+  const int r0 = req_row_ptr[b];
+  const int r1 = req_row_ptr[b + 1];
+  const int tid = threadIdx.x;
+
+  int nmax = 0;
+  for (int r = r0; r < r1; ++r) nmax = max(nmax, (row_pos[r] + 1) / c);
+  nmax = min(nmax, max_vis);
+  if (blockIdx.x == 0 && row_len != nullptr)
+    for (int r = r0 + tid; r < r1; r += blockDim.x) row_len[r] = max(0, min((row_pos[r] + 1) / c, max_vis));
+
+  const int j0 = blockIdx.x * chunk;
+  if (j0 >= nmax) return;
+  const int j1 = min(j0 + chunk, nmax);
+  const int per_page = kPage / c;
+  const int sub = tid & 15;  // 16-byte slice: dims 8*sub .. 8*sub+7
+  const int kin = tid >> 4;  // key within a 16-key round
+  const int32_t* pt = page_table + (int64_t)b * pt_stride;
+
+  for (int g0 = r0; g0 < r1; g0 += RG) {
+    const int ng = min(RG, r1 - g0);
+    u32x4_t qv[RG][kHeads];
+    int nvis[RG];
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      if (i < ng) {
+        const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(q + (int64_t)(g0 + i) * kHeads * kDim) + sub;
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) qv[i][h] = qp[h * (kDim / 8)];
+        nvis[i] = min((row_pos[g0 + i] + 1) / c, max_vis);
+      } else {
+#pragma unroll
+        for (int h = 0; h < kHeads; ++h) qv[i][h] = u32x4_t{0u, 0u, 0u, 0u};
+        nvis[i] = 0;
+      }
+    }
+
+    for (int jr = j0; jr < j1; jr += 16 * U) {
+      u32x4_t kv[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int jb = jr + 16 * u;  // 16-aligned: the round lies in one page
+        const int j = jb + kin;
+        kv[u] = u32x4_t{0u, 0u, 0u, 0u};
+        ok[u] = true;
+        if (jb < j1) {
+          const int32_t page = pt[(c * jb) >> 6];
+          ok[u] = page >= 0 && page < num_pages;
+          if (ok[u] && j < j1) {
+            const int64_t slot = (int64_t)page * per_page + (j & (per_page - 1));
+            kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kcache + slot * kDim) + sub);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = jr + 16 * u + kin;
+#pragma unroll
+        for (int i = 0; i < RG; ++i) {
+          if (i < ng) {
+            const float s = row_head_relu_sum(slice_dot(kv[u], qv[i][0]), slice_dot(kv[u], qv[i][1]),
+                                              slice_dot(kv[u], qv[i][2]), slice_dot(kv[u], qv[i][3]), sub);
+            if (sub == 0 && j < j1 && j < nvis[i])
+              scores[(int64_t)(g0 + i) * ld + j] = ok[u] ? s * kScale : __builtin_nanf("");
+          }
+        }
+      }
+    }
+  }
+}
+
+static int pick_rg(int num_rows, int num_req) {
+  const int avg = (num_rows + num_req - 1) / num_req;
+  return avg <= 1 ? 1 : avg <= 2 ? 2 : avg <= 4 ? 4 : 8;
+}
+
+int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_pages,
+                        const int32_t* page_table, int32_t pt_stride,
+                        const int32_t* req_row_ptr, int32_t num_req,
+                        const int32_t* row_pos, int32_t num_rows,
+                        int32_t c, int32_t max_vis,
+                        float* scores, int64_t ld, int32_t* row_len, hipStream_t stream) {
+  constexpr int U = 4;
+  // Chunk: a multiple of one unrolled round (64 keys), sized so a launch has
+  // a few thousand workgroups when the batch is large.
+  const int64_t keys = (int64_t)max_vis * num_req;
+  int64_t chunk = (keys / 2048 + 63) / 64 * 64;
+  chunk = chunk < 64 ? 64 : (chunk > 4096 ? 4096 : chunk);
+  const int nchunks = max_vis > 0 ? (int)((max_vis + chunk - 1) / chunk) : 1;
+  dim3 grid(nchunks, num_req), block(256);
+  const int rg = pick_rg(num_rows, num_req);
+#define BS_LAUNCH_DECODE(RGV)                                                                 \
+  hipLaunchKernelGGL((score_decode_kernel<RGV, U>), grid, block, 0, stream, q, kcache, num_pages, \
+                     page_table, pt_stride, req_row_ptr, row_pos, c, max_vis, (int32_t)chunk,    \
+                     scores, ld, row_len)
+  switch (rg) {
+    case 1: BS_LAUNCH_DECODE(1); break;
+    case 2: BS_LAUNCH_DECODE(2); break;
+    case 4: BS_LAUNCH_DECODE(4); break;
+    default: BS_LAUNCH_DECODE(8); break;
+  }
+#undef BS_LAUNCH_DECODE
+  return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
+}
+
+}  // namespace bs

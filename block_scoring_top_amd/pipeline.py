@@ -1,0 +1,60 @@
+"""The whole hot path on one GPU: score -> top-k -> expand/translate.
+
+Allocates the output and workspace tensors once (torch, device memory) and
+then enqueues the three C-ABI calls on the current stream.  No host
+synchronisation happens inside :meth:`IndexerPath.run`.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (idx_expand_translate, idx_score_decode, idx_score_prefill, topk_select_rows,
+               topk_workspace)
+
+
+class IndexerPath:
+    """Buffers for one batch shape plus the three calls.
+
+    ``inp`` is any object with the device-input fields (c, k, q, kcache,
+    num_pages, page_table, req_row_ptr, row_pos, max_vis), e.g.
+    ``synth.device.DeviceInputs``.  ``scorer`` is "decode" or "prefill".
+    """
+
+    def __init__(self, inp, scorer: str = "decode"):
+        if scorer not in ("decode", "prefill"):
+            raise ValueError("scorer must be 'decode' or 'prefill'")
+        self.inp = inp
+        self.scorer = scorer
+        dev = inp.q.device
+        R = int(inp.row_pos.shape[0])
+        ld = max(int(inp.max_vis), 1)
+        ld = (ld + 3) // 4 * 4  # 16-byte aligned rows
+        self.scores = torch.empty((R, ld), dtype=torch.float32, device=dev)
+        self.row_len = torch.empty(R, dtype=torch.int32, device=dev)
+        self.sel = torch.empty((R, inp.k), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty(R, dtype=torch.int32, device=dev)
+        ld_out = inp.k * inp.c + inp.c - 1
+        self.slots = torch.empty((R, ld_out), dtype=torch.int32, device=dev)
+        self.pos = torch.empty((R, ld_out), dtype=torch.int32, device=dev)
+        self.out_count = torch.empty(R, dtype=torch.int32, device=dev)
+        self.workspace = topk_workspace(R, int(inp.max_vis), inp.k, dev)
+
+    def score(self, stream=None):
+        i = self.inp
+        fn = idx_score_decode if self.scorer == "decode" else idx_score_prefill
+        fn(i.q, i.kcache, i.num_pages, i.page_table, i.req_row_ptr, i.row_pos, i.c, i.max_vis,
+           self.scores, self.row_len, stream=stream)
+
+    def select(self, stream=None):
+        topk_select_rows(self.scores, self.row_len, int(self.inp.max_vis), self.inp.k, self.sel,
+                         self.sel_count, self.workspace, stream=stream)
+
+    def expand(self, stream=None):
+        i = self.inp
+        idx_expand_translate(self.sel, self.sel_count, i.k, i.req_row_ptr, i.row_pos, i.c, i.page_table,
+                             self.slots, self.out_count, out_pos=self.pos, stream=stream)
+
+    def run(self, stream=None):
+        self.score(stream)
+        self.select(stream)
+        self.expand(stream)

@@ -1,0 +1,206 @@
+/*
+ * blockscore.h - C ABI of the MI355X (gfx950) sparse-attention indexer hot path.
+ *
+ * The path has three steps, each one call:
+ *   1. score   - idx_score_decode / idx_score_prefill
+ *   2. select  - topk_select_rows
+ *   3. expand  - idx_expand_translate
+ *
+ * Sources (pages on the subject):
+ *   [QSA]   "Qwen3.8-Flash-Next Day-0 in SGLang" (theainews.cc), section on Qwen
+ *           sparse attention (QSA): 4 indexer query heads of 128 dims and one
+ *           shared key head; one bf16 compressed index key per 4 tokens; the
+ *           score equation s_{t,b}; top-512 blocks expanded to 2048 positions
+ *           plus the 0-3 tokens of the unfinished block (at most 2051); page-
+ *           aligned full_slot/4 addressing of the compressed cache; a paged
+ *           version of the same scorer for decode and a custom kernel for
+ *           prefill.
+ *   [TOPK]  GLM-5.2 on SGLang blog (aihot.virxact.com), Kernel Optimization >
+ *           TopK-V2, text and Figures 2-4: top-k as selection rather than sort
+ *           over FP32 score rows, runtime k up to 2048, exactly k results,
+ *           selected logical positions translated to physical KV-cache slots.
+ *   [MASK]  vllm-sparse-mla-blackwell (shadowgraph.io), Design notes: the only
+ *           mask downstream is an index >= 0 sentinel, so padding is -1.
+ *   [SYNC]  GLM-5.2 blog, Runtime Optimization: the indexer path carries no
+ *           device-to-host synchronisation; [QSA]: the metadata path is graph-
+ *           compatible and may run on a second stream.
+ *
+ * Conventions for every call:
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or synchronises; every call is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL = the default stream) and
+ *     returns at once.  Outputs are valid once the stream reaches the call.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     failure the call returns a negative bs_status and launches nothing.
+ *     HIP launch failures return BS_ERR_LAUNCH.
+ *   - num_rows == 0 (or num_req == 0) is a no-op that returns BS_OK.
+ *   - Device-resident data (positions, page ids, lengths, selections) is not
+ *     read back to the host.  Its preconditions are stated per call; the
+ *     kernels clamp every index so that a violation never reads or writes
+ *     outside the buffers described by the host-side sizes, but the values
+ *     produced for violating rows are then unspecified.
+ *   - There is no global state: calls are thread-safe.  Calls that share a
+ *     workspace must not overlap in time (use one stream).
+ *
+ * Shapes and layouts:
+ *   - bf16 values travel as their uint16 bit patterns.
+ *   - q:          [num_rows][4][128] bf16, row-major (1 KiB per row).
+ *   - kcache:     [num_pages * (64/c)][128] bf16.  Physical page p holds the
+ *                 compressed slots p*(64/c) .. p*(64/c) + 64/c - 1.  Block j of
+ *                 request b (covering tokens c*j .. c*j+c-1) lives at slot
+ *                 page_table[b][(c*j)/64] * (64/c) + j mod (64/c), which is the
+ *                 full slot of its first token divided by c [QSA].
+ *   - page_table: [num_req][pt_stride] int32, logical 64-token page -> physical
+ *                 page id in [0, num_pages); entries past a request's pages
+ *                 may hold -1.
+ *   - req_row_ptr:[num_req + 1] int32, non-decreasing, req_row_ptr[0] == 0 and
+ *                 req_row_ptr[num_req] == num_rows; rows of request b are
+ *                 req_row_ptr[b] .. req_row_ptr[b+1]-1.
+ *   - row_pos:    [num_rows] int32, the 0-based token position t of each query
+ *                 row.  The row sees tokens 0..t; its visible blocks are
+ *                 j < n_vis(t) = floor((t+1)/c) and its pending (unfinished
+ *                 block) tokens are c*n_vis .. t, 0 to c-1 of them.
+ */
+#ifndef BLOCKSCORE_H
+#define BLOCKSCORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bs_status {
+  BS_OK = 0,
+  BS_ERR_NULL = -1,      /* a required pointer is NULL */
+  BS_ERR_ARG = -2,       /* a size, stride, k or c is out of range */
+  BS_ERR_WORKSPACE = -3, /* workspace missing or smaller than topk_workspace_bytes() */
+  BS_ERR_LAUNCH = -4     /* the HIP runtime rejected a launch */
+};
+
+#define BS_HEADS 4        /* indexer query heads [QSA] */
+#define BS_DIM 128        /* head dimension [QSA] */
+#define BS_PAGE_TOKENS 64 /* tokens per KV page */
+#define BS_KMAX 2048      /* largest runtime k [TOPK] */
+
+/*
+ * idx_score_decode - paged block scores for decode / speculative-verify rows
+ * [QSA: the paged scorer used in decode].
+ *
+ * For every row r of request b and every visible block j < n_vis(row_pos[r]):
+ *   scores[r*ld_scores + j] =
+ *       (1/sqrt(128)) * sum_{h=0..3} max(0, <q[r][h][:], kbar_b[j][:]>)
+ * with kbar_b[j] read from kcache through the page table (layout above), bf16
+ * products accumulated in FP32.  Keys are streamed once per request and scored
+ * against all rows of that request.  Entries j >= n_vis(r) are not written.
+ *
+ *   c          compression ratio, 4 (QSA c4) or 1 (uncompressed, DSA style).
+ *   num_pages  physical pages in kcache (page ids outside [0, num_pages) are
+ *              not read; the scores of their blocks are unspecified).
+ *   max_vis    host-side bound: every row must have n_vis <= max_vis; the
+ *              kernels never score past it.  Requires max_vis <= ld_scores and
+ *              c*max_vis <= 64*pt_stride.
+ *   row_len    optional output [num_rows] int32: min(n_vis(r), max_vis), the
+ *              length topk_select_rows takes.  May be NULL.
+ * Device preconditions: row_pos[r] >= 0; page ids valid; rows of a request
+ * contiguous as given by req_row_ptr.
+ * Returns BS_OK, BS_ERR_NULL (q, kcache, page_table, req_row_ptr, row_pos or
+ * scores NULL with num_rows > 0), BS_ERR_ARG (c not 1 or 4, negative counts,
+ * pt_stride < 1, max_vis < 0, ld_scores < max_vis, c*max_vis > 64*pt_stride)
+ * or BS_ERR_LAUNCH.
+ */
+int idx_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_pages,
+                     const int32_t* page_table, int32_t pt_stride,
+                     const int32_t* req_row_ptr, int32_t num_req,
+                     const int32_t* row_pos, int32_t num_rows,
+                     int32_t c, int32_t max_vis,
+                     float* scores, int64_t ld_scores, int32_t* row_len,
+                     void* stream);
+
+/*
+ * idx_score_prefill - the same scores for prefill chunks, computed as a dense
+ * bf16 contraction on the matrix cores [QSA: the custom prefill index-score
+ * kernel].  Same arguments, layouts, outputs and errors as idx_score_decode;
+ * causal visibility per row (entries j >= n_vis(r) are not written).  Suited
+ * to requests with many rows; any row count is correct.
+ */
+int idx_score_prefill(const uint16_t* q, const uint16_t* kcache, int64_t num_pages,
+                      const int32_t* page_table, int32_t pt_stride,
+                      const int32_t* req_row_ptr, int32_t num_req,
+                      const int32_t* row_pos, int32_t num_rows,
+                      int32_t c, int32_t max_vis,
+                      float* scores, int64_t ld_scores, int32_t* row_len,
+                      void* stream);
+
+/*
+ * topk_workspace_bytes - device workspace topk_select_rows needs for
+ * (num_rows, max_len, k).  0 means no workspace is needed (NULL may be
+ * passed).  The workspace must be zero-filled before its first use; every call
+ * leaves it zero-filled again, so one zero-fill at allocation suffices.
+ */
+size_t topk_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k);
+
+/*
+ * topk_select_rows - exact top-k per FP32 score row [TOPK].
+ *
+ * For each row r with n = min(row_len[r], max_len) entries scores[r*ld+0..n-1],
+ * selects m = min(k, n) indices: those of the m largest scores, equal scores
+ * going to the lower index (-0.0 equals +0.0).  The result is unique.
+ *   sel        output [num_rows][k] int32: the m chosen indices in unspecified
+ *              order, then -1 padding.
+ *   sel_count  output [num_rows] int32: m.
+ *   max_len    host-side bound on row_len (capacity); ld_scores >= max_len.
+ *   k          1 .. 2048.
+ * Method: a selection, not a sort.  FP32 scores are rounded to FP16, mapped
+ * to an order-preserving 16-bit key whose upper 10 bits index a 1,024-bin
+ * histogram; the bin holding the m-th largest is located, entries in higher
+ * bins are emitted directly, and the boundary bin is resolved exactly on the
+ * (FP32 key, index) pair by radix selection.  Short rows are kept in
+ * registers, medium rows stream through one workgroup, long rows are split
+ * over several workgroups whose histograms merge through device-scope atomics.
+ * Device preconditions: row_len[r] >= 0 (negative counts as 0); no NaN
+ * (a NaN is ordered above +inf or below -inf by its sign bit).
+ * Returns BS_OK, BS_ERR_NULL, BS_ERR_ARG (k outside 1..2048, max_len < 0,
+ * ld_scores < max_len), BS_ERR_WORKSPACE or BS_ERR_LAUNCH.
+ */
+int topk_select_rows(const float* scores, int64_t ld_scores, const int32_t* row_len,
+                     int32_t num_rows, int32_t max_len, int32_t k,
+                     int32_t* sel, int32_t* sel_count,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * idx_expand_translate - expand chosen blocks to token positions, append the
+ * pending tokens and translate to physical KV slots [QSA, TOPK, MASK].
+ *
+ * For row r of request b at position t with m = min(max(sel_count[r], 0), k):
+ *   each chosen block j = sel[r*k + i] (i < m) becomes positions
+ *   c*j .. c*j+c-1 (in that order, blocks in the order given), then the
+ *   pending positions c*n_vis(t) .. t follow; out_count[r] = c*m + p.
+ *   out_slots[r*ld_out + i] = page_table[b][pos/64] * 64 + pos mod 64.
+ *   out_pos (optional, may be NULL) receives the logical positions.
+ *   Entries past out_count[r] are -1.  A chosen index outside [0, n_vis) or a
+ *   position whose page entry is negative yields -1 in its place.
+ *   ld_out >= k*c + c - 1 (2051 for c = 4, k = 512).
+ * Returns BS_OK, BS_ERR_NULL, BS_ERR_ARG (k outside 1..2048, c not 1 or 4,
+ * ld_out too small, negative counts, pt_stride < 1, num_req == 0 while
+ * num_rows > 0) or BS_ERR_LAUNCH.
+ */
+int idx_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_t k,
+                         const int32_t* req_row_ptr, int32_t num_req,
+                         const int32_t* row_pos, int32_t num_rows, int32_t c,
+                         const int32_t* page_table, int32_t pt_stride,
+                         int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
+                         int32_t ld_out, void* stream);
+
+/* bs_status_string - a static, human-readable name for a status code. */
+const char* bs_status_string(int status);
+
+/* bs_abi_version - version of this ABI (1). */
+int bs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKSCORE_H */

@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports every symbol include/*.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes as C
+import glob
+import os
+import re
+
+import pytest
+
+import block_scoring_top_amd as bst
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+BS_OK, BS_ERR_NULL, BS_ERR_ARG, BS_ERR_WORKSPACE = 0, -1, -2, -3
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for want in ("idx_score_decode", "idx_score_prefill", "topk_select_rows", "idx_expand_translate",
+                 "topk_workspace_bytes", "bs_status_string", "bs_abi_version"):
+        assert want in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    L = bst.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    assert bst.lib().bs_abi_version() == 1
+    assert bst.status_string(BS_OK) == "BS_OK"
+    for s in (BS_ERR_NULL, BS_ERR_ARG, BS_ERR_WORKSPACE, -4):
+        assert bst.status_string(s).startswith("BS_ERR")
+    assert bst.status_string(12345) == "unknown status"
+
+
+P = C.c_void_p
+NULL = None
+FAKE = C.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def _score(fn, **kw):
+    a = dict(q=FAKE, kc=FAKE, num_pages=1, pt=FAKE, pt_stride=1, ptr=FAKE, num_req=1, pos=FAKE, num_rows=1,
+             c=4, max_vis=16, scores=FAKE, ld=16, row_len=NULL, stream=NULL)
+    a.update(kw)
+    return getattr(bst.lib(), fn)(a["q"], a["kc"], a["num_pages"], a["pt"], a["pt_stride"], a["ptr"], a["num_req"],
+                                  a["pos"], a["num_rows"], a["c"], a["max_vis"], a["scores"], a["ld"],
+                                  a["row_len"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["idx_score_decode", "idx_score_prefill"])
+def test_score_validation(fn):
+    assert _score(fn, num_rows=0) == BS_OK          # no-op, nothing launched
+    assert _score(fn, num_req=0) == BS_OK
+    assert _score(fn, c=3) == BS_ERR_ARG
+    assert _score(fn, c=2) == BS_ERR_ARG
+    assert _score(fn, num_rows=-1) == BS_ERR_ARG
+    assert _score(fn, max_vis=-1) == BS_ERR_ARG
+    assert _score(fn, ld=15) == BS_ERR_ARG          # ld < max_vis
+    assert _score(fn, pt_stride=0) == BS_ERR_ARG
+    assert _score(fn, max_vis=17) == BS_ERR_ARG     # 4*17 tokens > one 64-token page
+    assert _score(fn, c=1, max_vis=65, ld=65) == BS_ERR_ARG
+    for k in ("q", "kc", "pt", "ptr", "pos", "scores"):
+        assert _score(fn, **{k: NULL}) == BS_ERR_NULL, k
+
+
+def _topk(**kw):
+    a = dict(scores=FAKE, ld=100000, row_len=FAKE, num_rows=2, max_len=100000, k=2048, sel=FAKE, cnt=FAKE,
+             ws=FAKE, ws_bytes=1 << 30, stream=NULL)
+    a.update(kw)
+    return bst.lib().topk_select_rows(a["scores"], a["ld"], a["row_len"], a["num_rows"], a["max_len"], a["k"],
+                                      a["sel"], a["cnt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_topk_validation():
+    assert _topk(num_rows=0) == BS_OK
+    assert _topk(k=0) == BS_ERR_ARG
+    assert _topk(k=2049) == BS_ERR_ARG
+    assert _topk(max_len=-1) == BS_ERR_ARG
+    assert _topk(ld=99999) == BS_ERR_ARG
+    for k in ("scores", "row_len", "sel", "cnt"):
+        assert _topk(**{k: NULL}) == BS_ERR_NULL, k
+    need = bst.topk_workspace_bytes(2, 100000, 2048)
+    assert need > 0
+    assert _topk(ws=NULL) == BS_ERR_WORKSPACE
+    assert _topk(ws_bytes=need - 1) == BS_ERR_WORKSPACE
+
+
+def test_topk_workspace_sizes():
+    assert bst.topk_workspace_bytes(0, 100000, 2048) == 0
+    assert bst.topk_workspace_bytes(8192, 16384, 512) == 0       # single-workgroup rows need none
+    a = bst.topk_workspace_bytes(8, 81920, 2048)
+    b = bst.topk_workspace_bytes(16, 81920, 2048)
+    assert a > 0 and b == 2 * a
+
+
+def _expand(**kw):
+    a = dict(sel=FAKE, cnt=FAKE, k=512, ptr=FAKE, num_req=1, pos=FAKE, num_rows=1, c=4, pt=FAKE, pt_stride=1,
+             slots=FAKE, opos=NULL, ocnt=FAKE, ld_out=2051, stream=NULL)
+    a.update(kw)
+    return bst.lib().idx_expand_translate(a["sel"], a["cnt"], a["k"], a["ptr"], a["num_req"], a["pos"],
+                                          a["num_rows"], a["c"], a["pt"], a["pt_stride"], a["slots"], a["opos"],
+                                          a["ocnt"], a["ld_out"], a["stream"])
+
+
+def test_expand_validation():
+    assert _expand(num_rows=0) == BS_OK
+    assert _expand(ld_out=2050) == BS_ERR_ARG           # needs k*c + c - 1 = 2051
+    assert _expand(c=1, ld_out=2047, k=2048) == BS_ERR_ARG
+    assert _expand(k=0) == BS_ERR_ARG
+    assert _expand(k=2049, ld_out=10000) == BS_ERR_ARG
+    assert _expand(c=2) == BS_ERR_ARG
+    assert _expand(num_req=0) == BS_ERR_ARG
+    assert _expand(pt_stride=0) == BS_ERR_ARG
+    for k in ("sel", "cnt", "ptr", "pos", "pt", "slots", "ocnt"):
+        assert _expand(**{k: NULL}) == BS_ERR_NULL, k
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(bst, "_lib", None)
+    monkeypatch.setattr(bst, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(bst.BlockScoreError):
+        bst.lib()
+
+
+def test_product_path_does_not_import_the_oracle():
+    # The HIP path must never route through the CPU oracle.
+    for path in glob.glob(os.path.join(ROOT, "block_scoring_top_amd", "**", "*"), recursive=True):
+        if path.endswith((".py", ".hip", ".h", ".cpp")):
+            text = open(path).read()
+            assert "import oracle" not in text and "from oracle" not in text, path
+            assert "liboracle" not in text, path

@@ -1,0 +1,245 @@
+"""HIP path vs the CPU oracle, through the C ABI, on seeded inputs.
+
+Bars: scores within 1e-4*(1+|s|); top-k on given FP32 rows identical; top-k
+on the GPU's own scores identical to the oracle's top-k of those same scores;
+end-to-end selections differing only within 2e-4 of the k-th oracle score;
+expand/translate of a given selection identical in canonical form.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from checkers import (check_expand_exact, check_scores, check_topk_e2e, check_topk_exact)
+
+pytestmark = pytest.mark.gpu
+
+gu = pytest.importorskip("gpu_util")
+
+
+def _full_check(inp, scorer="decode"):
+    """Every stage against the oracle: scores (tolerance), top-k of the GPU
+    scores (exact), end-to-end selection (band), expand of the GPU selection
+    (exact)."""
+    g = gu.run_path(inp, scorer)
+    ref = oracle.pipeline(inp)
+    assert np.array_equal(g["row_len"], ref["row_len"])
+    check_scores(g["scores"], ref["scores"], ref["row_len"])
+    ld = max(inp.max_vis, 1)
+    sel_on_gpu_scores, cnt_on_gpu_scores = oracle.topk(np.ascontiguousarray(g["scores"][:, :ld]), g["row_len"], inp.k)
+    check_topk_exact(g["sel"], g["sel_count"], sel_on_gpu_scores, cnt_on_gpu_scores)
+    swaps = check_topk_e2e(g["sel"], g["sel_count"], ref["scores"], ref["sel"], ref["sel_count"], ref["row_len"])
+    slots, pos, oc = oracle.expand_translate(inp, g["sel"], g["sel_count"])
+    check_expand_exact(g["slots"], g["pos"], g["out_count"], slots, pos, oc, gu.pending_counts(inp))
+    return swaps
+
+
+# ---------------------------------------------------------------------------
+# Decode scorer
+# ---------------------------------------------------------------------------
+
+def test_decode_cfg_qsa_1x8k_end_to_end():
+    _full_check(synth.qsa_decode_1x8k())
+
+
+def test_decode_verify_small_ragged():
+    _full_check(synth.qsa_verify_64req(B=8, lo=300, hi=20000))
+
+
+def test_decode_dsa_small():
+    _full_check(synth.dsa_decode_16x80k(B=3, L=5000))
+
+
+def test_decode_edge_rows():
+    # rows with 0 visible blocks, 1 block, page boundaries; a request with no
+    # rows; a request with 11 rows (more than one row group).
+    rng = np.random.default_rng(101)
+    rows = [[0, 1, 2], [3, 4, 5, 62, 63, 64, 65, 66, 67], [], [400 + i for i in range(11)]]
+    inp = synth.build_paged_batch("edge", 101, c=4, k=8, ctx_tokens=[3, 68, 1, 411], row_pos_per_req=rows, rng=rng)
+    _full_check(inp)
+    inp1 = synth.build_paged_batch("edge1", 102, c=1, k=8, ctx_tokens=[3, 68, 1, 411], row_pos_per_req=rows, rng=rng)
+    _full_check(inp1)
+
+
+def test_decode_power_of_two_scaling_exact():
+    # s(2q) == 2*s(q) bit for bit in any fixed accumulation order.
+    inp = synth.qsa_verify_64req(B=4, lo=1000, hi=9000)
+    s1, l1 = gu.gpu_scores(inp)
+    q2 = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp.q) * np.float32(2.0))
+    s2, l2 = gu.gpu_scores(synth.IndexerInputs(**{**inp.__dict__, "q": q2}))
+    for r in range(inp.num_rows):
+        n = l1[r]
+        assert np.array_equal(s2[r, :n], np.float32(2.0) * s1[r, :n])
+
+
+def test_decode_leaves_invisible_entries_untouched():
+    inp = synth.qsa_verify_64req(B=5, lo=500, hi=6000)
+    s, rl = gu.gpu_scores(inp, ld=inp.max_vis + 40)
+    for r in range(inp.num_rows):
+        assert np.all(np.isfinite(s[r, :rl[r]]))
+        assert np.all(np.isnan(s[r, rl[r]:]))
+
+
+# ---------------------------------------------------------------------------
+# Top-k on given FP32 rows: bit-exact
+# ---------------------------------------------------------------------------
+
+def test_topk_cfg_8x80k_exact():
+    w = synth.topk_8x80k()
+    (out,), _ = gu.gpu_topk(w.scores, w.row_len, w.k)
+    ref_sel, ref_cnt = oracle.topk(w.scores, w.row_len, w.k)
+    check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
+
+
+@pytest.mark.parametrize("n", [1, 7, 511, 512, 513, 2047, 2048, 2049, 4096, 16383, 16384, 16385, 32768, 32769,
+                               50000])
+def test_topk_lengths_and_tie_storms(n):
+    rows = synth.tie_storm_rows(1000 + n, 8, n)
+    rng = np.random.default_rng(n)
+    rows = np.concatenate([rows, rng.standard_normal((2, n)).astype(np.float32)])
+    lens = np.full(rows.shape[0], n, dtype=np.int32)
+    for k in (1, 512, 2048):
+        (out,), _ = gu.gpu_topk(rows, lens, k)
+        ref_sel, ref_cnt = oracle.topk(rows, lens, k)
+        check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
+
+
+def test_topk_mixed_lengths_one_launch():
+    # one launch mixing every path: take-all, register, streaming, multi-workgroup
+    rng = np.random.default_rng(7)
+    ld = 90000
+    lens = np.array([0, 1, 100, 511, 512, 600, 5000, 16384, 16385, 30000, 32768, 32769, 45000, 81920, 90000],
+                    dtype=np.int32)
+    rows = rng.standard_normal((lens.shape[0], ld)).astype(np.float32)
+    rows[3] = 1.0
+    rows[9, ::3] = 0.25
+    for k in (512, 2048):
+        (out,), _ = gu.gpu_topk(rows, lens, k)
+        ref_sel, ref_cnt = oracle.topk(rows, lens, k)
+        check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
+
+
+def test_topk_overflowing_boundary_bin():
+    # more than 4,096 entries tie in the boundary bin: exercises the re-scan refinement
+    rng = np.random.default_rng(8)
+    for n in (12000, 30000, 70000):
+        rows = np.empty((3, n), dtype=np.float32)
+        rows[0] = np.float32(1.0) + rng.integers(0, 16, n).astype(np.float32) * np.float32(2.0 ** -20)
+        rows[1] = np.float32(3.0)
+        rows[2] = rng.choice(np.array([0.5, 0.5000001, 0.50000006], dtype=np.float32), n)
+        lens = np.full(3, n, dtype=np.int32)
+        for k in (1, 2048):
+            (out,), _ = gu.gpu_topk(rows, lens, k)
+            ref_sel, ref_cnt = oracle.topk(rows, lens, k)
+            check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
+
+
+def test_topk_repeat_determinism_and_workspace_reset():
+    w = synth.topk_8x80k(seed=77)
+    outs, ws = gu.gpu_topk(w.scores, w.row_len, w.k, reps=20)
+    ref_sel, ref_cnt = oracle.topk(w.scores, w.row_len, w.k)
+    for sel, cnt in outs:
+        check_topk_exact(sel, cnt, ref_sel, ref_cnt)
+    assert int(ws.count_nonzero().item()) == 0, "workspace must be left zero-filled"
+    # another batch through the same workspace
+    w2 = synth.topk_8x80k(seed=78)
+    (out,), _ = gu.gpu_topk(w2.scores, w2.row_len, w2.k, workspace=ws)
+    r2 = oracle.topk(w2.scores, w2.row_len, w2.k)
+    check_topk_exact(out[0], out[1], *r2)
+
+
+def test_topk_qsa_score_rows():
+    # real QSA-shaped score rows (non-negative, many exact zeros)
+    inp = synth.qsa_verify_64req(B=6, lo=20000, hi=131072)
+    scores, rl = oracle.score(inp)
+    scores = np.nan_to_num(scores, nan=-1.0)
+    (out,), _ = gu.gpu_topk(scores, rl, 512, max_len=inp.max_vis)
+    ref = oracle.topk(scores, rl, 512)
+    check_topk_exact(out[0], out[1], *ref)
+
+
+# ---------------------------------------------------------------------------
+# Expand / translate: exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("c", [1, 4])
+def test_expand_exact_on_oracle_selection(c):
+    inp = (synth.qsa_verify_64req(B=7, lo=200, hi=30000) if c == 4 else synth.dsa_decode_16x80k(B=2, L=6000))
+    ref = oracle.pipeline(inp)
+    # scramble the order within each selection: the output order is free
+    sel = ref["sel"].copy()
+    rng = np.random.default_rng(5)
+    for r in range(sel.shape[0]):
+        m = ref["sel_count"][r]
+        sel[r, :m] = rng.permutation(sel[r, :m])
+    slots, pos, oc = gu.gpu_expand(inp, sel, ref["sel_count"])
+    check_expand_exact(slots, pos, oc, ref["slots"], ref["pos"], ref["out_count"], gu.pending_counts(inp))
+
+
+def test_expand_invalid_entries_become_sentinels():
+    inp = synth.qsa_decode_1x8k()
+    sel = np.full((1, inp.k), -1, dtype=np.int32)
+    sel[0, :4] = [5, -1, 2048, 7]  # -1 and the unfinished block 2048 are invalid
+    slots, pos, oc = gu.gpu_expand(inp, sel, np.array([4], dtype=np.int32))
+    assert oc[0] == 4 * 4 + 2
+    assert np.all(slots[0, 4:12] == -1) and np.all(pos[0, 4:12] == -1)
+    assert pos[0, :4].tolist() == [20, 21, 22, 23] and pos[0, 12:16].tolist() == [28, 29, 30, 31]
+    assert pos[0, 16:18].tolist() == [8192, 8193]
+    assert np.all(slots[0, 18:] == -1)
+
+
+# ---------------------------------------------------------------------------
+# End to end at the full workload sizes
+# ---------------------------------------------------------------------------
+
+def test_e2e_verify_64req_full():
+    _full_check(synth.qsa_verify_64req())
+
+
+def test_e2e_dsa_16x80k_full():
+    _full_check(synth.dsa_decode_16x80k())
+
+
+# ---------------------------------------------------------------------------
+# Prefill scorer (matrix cores)
+# ---------------------------------------------------------------------------
+
+def test_prefill_small_vs_oracle():
+    _full_check(synth.qsa_prefill_8k(rows=200, ctx=3001), scorer="prefill")
+
+
+def test_prefill_multi_request_ragged():
+    rng = np.random.default_rng(55)
+    rows = [list(range(900, 1000)), [5, 6, 7], list(range(2000, 2077)), []]
+    inp = synth.build_paged_batch("pf", 55, c=4, k=64, ctx_tokens=[1000, 8, 2077, 10], row_pos_per_req=rows,
+                                  rng=rng)
+    _full_check(inp, scorer="prefill")
+
+
+def test_prefill_full_size_sampled_rows():
+    # The full 8192-row prefill in the benchmark's launch shape; the oracle
+    # checks a sample of rows one by one.
+    inp = synth.qsa_prefill_8k()
+    g = gu.run_path(inp, "prefill")
+    rng = np.random.default_rng(3)
+    sample = np.sort(np.concatenate([[0, 1, 63, 64, 4095, 8191], rng.choice(8192, 40, replace=False)]))
+    sub = synth.IndexerInputs(**{**inp.__dict__, "q": inp.q[sample], "row_pos": inp.row_pos[sample],
+                                 "req_row_ptr": np.array([0, sample.size], dtype=np.int32)})
+    ref = oracle.pipeline(sub)
+    assert np.array_equal(g["row_len"][sample], ref["row_len"])
+    check_scores(g["scores"][sample], ref["scores"], ref["row_len"])
+    check_topk_e2e(g["sel"][sample], g["sel_count"][sample], ref["scores"], ref["sel"], ref["sel_count"],
+                   ref["row_len"])
+    slots, pos, oc = oracle.expand_translate(sub, g["sel"][sample], g["sel_count"][sample])
+    check_expand_exact(g["slots"][sample], g["pos"][sample], g["out_count"][sample], slots, pos, oc,
+                       gu.pending_counts(sub))
+
+
+def test_prefill_agrees_with_decode_scorer():
+    inp = synth.qsa_prefill_8k(rows=130, ctx=5000)
+    a, la = gu.gpu_scores(inp, "prefill")
+    b, lb = gu.gpu_scores(inp, "decode")
+    assert np.array_equal(la, lb)
+    check_scores(a, b.astype(np.float64), la, what="prefill vs decode")
