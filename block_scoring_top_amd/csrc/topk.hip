@@ -20,11 +20,12 @@
 //     device-scope atomics (first launch).  In the second launch every
 //     chunk's workgroup reads the merged histogram, finds the threshold bin,
 //     emits its own above-threshold entries through a global atomic cursor and
-//     appends its boundary candidates to a workspace list; the last workgroup
-//     of the row to arrive (a device-scope atomic counter with release/acquire
-//     fences) resolves the boundary bin and restores the row's workspace to
-//     zero.  No workgroup ever waits on another, so co-residency is never
-//     assumed.
+//     appends its boundary candidates to a workspace list.  A third launch
+//     (one workgroup per row) resolves the boundary bin and restores the
+//     row's workspace to zero.  The hand-offs sit at kernel boundaries: an
+//     in-kernel device-scope fence on gfx950 writes back and invalidates the
+//     per-XCD L2, which costs far more than a launch; and no workgroup ever
+//     waits on another, so co-residency is never assumed.
 #include "device.h"
 #include "kernels.h"
 
@@ -36,12 +37,13 @@ constexpr int kTkVpt = 16;                         // register path: values per 
 constexpr int kTkShortMax = kTkBlock * kTkVpt;     // 16,384
 constexpr int kTkLongMin = 32769;                  // rows this long use several workgroups
 constexpr int kTkChunk = 4096;                     // entries per workgroup on long rows
+static_assert(kTkChunk % kTkBlock == 0, "a long-row chunk is a whole number of passes");
 constexpr int kTkCand = 4096;                      // boundary candidates kept in LDS / workspace
 
 // Workspace record per row (long rows only): merged histogram, counters,
 // candidate list.
 constexpr size_t kWsHist = 0;
-constexpr size_t kWsCtr = kBins * 4;               // [0] emit cursor, [1] candidates, [2] arrivals
+constexpr size_t kWsCtr = kBins * 4;  // [0] emit cursor, [1] candidates, [2] threshold bin, [3] count above it
 constexpr size_t kWsCand = kWsCtr + 64;
 constexpr size_t kWsRow = kWsCand + (size_t)kTkCand * 8;
 
@@ -55,7 +57,7 @@ struct TopkShared {
   uint32_t ncand;
   uint32_t T;
   uint32_t above;
-  int last;
+  uint32_t base_up, base_cand;
 };
 
 __device__ __forceinline__ uint64_t composite_key(float v, int idx) {
@@ -305,47 +307,91 @@ __global__ __launch_bounds__(kTkBlock) void topk_main_kernel(
   else select_row<false>(s, row, n, m, out);
 }
 
-__global__ __launch_bounds__(kTkBlock) void topk_long_kernel(
+// Long rows, second launch: every chunk's workgroup finds the threshold bin
+// from the merged histogram, emits its above-threshold entries and appends
+// its boundary candidates to the row's workspace list.
+__global__ __launch_bounds__(kTkBlock) void topk_long_emit_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
-    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws) {
+    int32_t k, int32_t* __restrict__ sel, uint8_t* __restrict__ ws) {
   __shared__ TopkShared s;
   const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x;
   const int n = max(0, min(row_len[r], max_len));
   if (n < kTkLongMin) return;
-  const int nchunk = (n + kTkChunk - 1) / kTkChunk;
-  if (w >= nchunk) return;
+  if (w * kTkChunk >= n) return;
   const int m = k;  // n > 2048 >= k
+  const float* row = scores + (int64_t)r * ld;
+  int32_t* out = sel + (int64_t)r * k;
+  uint8_t* rec = ws_row(ws, r);
+  const uint32_t* gh = reinterpret_cast<const uint32_t*>(rec + kWsHist);
+  uint32_t* ctr = reinterpret_cast<uint32_t*>(rec + kWsCtr);
+  uint64_t* gcand = reinterpret_cast<uint64_t*>(rec + kWsCand);
+
+  s.hist[tid] = gh[tid];
+  if (tid == 0) {
+    s.emit = 0;
+    s.ncand = 0;
+  }
+  __syncthreads();
+  find_threshold(s.hist, kBins, (uint32_t)m, s);
+  const uint32_t T = s.T;
+  if (w == 0 && tid == 0) {
+    ctr[2] = T;
+    ctr[3] = s.above;
+  }
+  // Reserve output positions inside the workgroup first (LDS atomics), then
+  // one device-scope atomic per list for the whole workgroup: same-address
+  // device atomics serialise, so per-wave reservations would queue up.
+  const int lo = w * kTkChunk, hi = min(n, lo + kTkChunk);
+  constexpr int kPer = kTkChunk / kTkBlock;
+  float x[kPer];
+  bool up[kPer], eq[kPer];
+  uint32_t lup[kPer], lcand[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = lo + i * kTkBlock + tid;
+    const bool valid = idx < hi;
+    x[i] = valid ? row[idx] : 0.0f;
+    const uint32_t b = bin_of(x[i]);
+    up[i] = valid && b > T;
+    eq[i] = valid && b == T;
+    lup[i] = wave_reserve(&s.emit, up[i]);
+    lcand[i] = wave_reserve(&s.ncand, eq[i]);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    s.base_up = s.emit ? atomicAdd(&ctr[0], s.emit) : 0u;
+    s.base_cand = s.ncand ? atomicAdd(&ctr[1], s.ncand) : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = lo + i * kTkBlock + tid;
+    const uint32_t pos = s.base_up + lup[i];
+    if (up[i] && pos < (uint32_t)m) out[pos] = idx;
+    const uint32_t cpos = s.base_cand + lcand[i];
+    if (eq[i] && cpos < (uint32_t)kTkCand) gcand[cpos] = composite_key(x[i], idx);
+  }
+}
+
+// Long rows, third launch: one workgroup per row resolves the boundary bin
+// from the candidate list (or by re-reading the row if the list overflowed)
+// and leaves the row's workspace zero-filled.  The kernel boundaries between
+// the three launches make every workgroup's writes visible without fences.
+__global__ __launch_bounds__(kTkBlock) void topk_long_finish_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
+    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws) {
+  __shared__ TopkShared s;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int n = max(0, min(row_len[r], max_len));
+  if (n < kTkLongMin) return;
+  const int m = k;
   const float* row = scores + (int64_t)r * ld;
   int32_t* out = sel + (int64_t)r * k;
   uint8_t* rec = ws_row(ws, r);
   uint32_t* gh = reinterpret_cast<uint32_t*>(rec + kWsHist);
   uint32_t* ctr = reinterpret_cast<uint32_t*>(rec + kWsCtr);
   uint64_t* gcand = reinterpret_cast<uint64_t*>(rec + kWsCand);
-
-  s.hist[tid] = gh[tid];
-  __syncthreads();
-  find_threshold(s.hist, kBins, (uint32_t)m, s);
-  const uint32_t T = s.T, above = s.above;
-  const int lo = w * kTkChunk, hi = min(n, lo + kTkChunk);
-  for (int base = lo; base < hi; base += kTkBlock) {
-    const int idx = base + tid;
-    const bool valid = idx < hi;
-    const float x = valid ? row[idx] : 0.0f;
-    const uint32_t b = bin_of(x);
-    const bool up = valid && b > T;
-    const uint32_t pos = wave_reserve(&ctr[0], up);
-    if (up && pos < (uint32_t)m) out[pos] = idx;
-    const bool eq = valid && b == T;
-    const uint32_t cpos = wave_reserve(&ctr[1], eq);
-    if (eq && cpos < (uint32_t)kTkCand) gcand[cpos] = composite_key(x, idx);
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s.last = atomicAdd(&ctr[2], 1u) == (uint32_t)(nchunk - 1);
-  __syncthreads();
-  if (!s.last) return;
-  __threadfence();
-  const uint32_t nc = __hip_atomic_load(&ctr[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t nc = ctr[1], T = ctr[2], above = ctr[3];
   const uint32_t need = (uint32_t)m - above;
   if (tid == 0) s.emit = above;
   if (nc <= (uint32_t)kTkCand)
@@ -354,9 +400,11 @@ __global__ __launch_bounds__(kTkBlock) void topk_long_kernel(
   if (nc <= (uint32_t)kTkCand) refine<false>(s, row, n, T, nc, need, out, m);
   else refine<true>(s, row, n, T, nc, need, out, m);
   if (tid == 0) sel_count[r] = m;
-  // Leave the row's workspace zeroed for the next call.
+  // Leave the row's workspace zero-filled for the next call.
   gh[tid] = 0;
   if (tid < 16) ctr[tid] = 0;
+  const int used = (int)min(nc, (uint32_t)kTkCand);
+  for (int i = tid; i < used; i += kTkBlock) gcand[i] = 0;
 }
 
 size_t topk_workspace_size(int32_t num_rows, int32_t max_len, int32_t /*k*/) {
@@ -373,8 +421,10 @@ int launch_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t
                      sel_count, ws);
   if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
   if (any_long) {
-    hipLaunchKernelGGL(topk_long_kernel, grid, block, 0, stream, scores, ld, row_len, max_len, k, sel,
-                       sel_count, ws);
+    hipLaunchKernelGGL(topk_long_emit_kernel, grid, block, 0, stream, scores, ld, row_len, max_len, k, sel, ws);
+    if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
+    hipLaunchKernelGGL(topk_long_finish_kernel, dim3(num_rows), block, 0, stream, scores, ld, row_len, max_len,
+                       k, sel, sel_count, ws);
     if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
   }
   return BS_OK;
