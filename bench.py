@@ -81,16 +81,138 @@ def measured_traffic(kernel: str, digest: str):
 
 def cpu_baseline(inp, min_seconds: float):
     import oracle
+    import synth
+    topk_only = isinstance(inp, synth.ScoreRows)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.pipeline(inp)
+        if topk_only:
+            oracle.topk(inp.scores, inp.row_len, inp.k)
+        else:
+            oracle.pipeline(inp)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or reps >= 5000:
             break
-    return {"value": inp.num_rows * reps / el, "unit": "rows/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{reps} full batches of the timed workload ({inp.num_rows} rows each) through "
-                      f"score + top-k (full sort) + expand/translate, {el:.1f} s"}
+    what = "top-k (full sort)" if topk_only else "score + top-k (full sort) + expand/translate"
+    return {"value": round(inp.num_rows * reps / el, 2), "unit": "rows/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full batches of the timed workload ({inp.num_rows} rows each) through {what}, "
+                      f"{el:.1f} s"}
+
+
+def time_steps(fns, K, warmup, stream, probe=0, probe_every=5):
+    """Runs the callables of a step K times after `warmup` untimed steps and
+    returns (ms per step, avg ms of fns[probe]).
+
+    The step time comes from two HIP events around all K steps.  fns[probe]
+    (the dominant kernel) is bracketed by its own pair of HIP events on every
+    `probe_every`-th step of the same timed region; every event is recorded on
+    `stream`, the stream all calls are launched on.  (An event marker costs the
+    GPU a few microseconds, so bracketing every kernel of every step would
+    inflate the step time.)"""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    probes = []
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        for j, f in enumerate(fns):
+            if j == probe and i % probe_every == 0:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                f()
+                b.record(stream)
+                probes.append((a, b))
+            else:
+                f()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_probe = float(np.mean([a.elapsed_time(b) for a, b in probes]))
+    return start.elapsed_time(end) / K, t_probe
+
+
+def kernel_breakdown(fns, K, stream):
+    """Average time of each callable, each bracketed by HIP events, in a
+    separate pass after the timed region (for the per-kernel report only)."""
+    import numpy as np
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        for j, f in enumerate(fns):
+            f()
+            e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(len(fns))]
+
+
+def run_workload(name, K, warmup, dev):
+    import torch
+
+    import block_scoring_top_amd as bst
+    import synth
+    from block_scoring_top_amd.pipeline import IndexerPath
+    from synth.device import upload
+
+    log(f"generating {name}")
+    inp = synth.WORKLOADS[name]()
+    stream = torch.cuda.current_stream(dev)
+    if isinstance(inp, synth.ScoreRows):
+        # top-k only on given FP32 rows
+        s = torch.from_numpy(inp.scores).to(dev)
+        rl = torch.from_numpy(inp.row_len).to(dev)
+        sel = torch.empty((inp.num_rows, inp.k), dtype=torch.int32, device=dev)
+        cnt = torch.empty(inp.num_rows, dtype=torch.int32, device=dev)
+        ws = bst.topk_workspace(inp.num_rows, inp.max_len, inp.k, dev)
+        ms, t_topk = time_steps([lambda: bst.topk_select_rows(s, rl, inp.max_len, inp.k, sel, cnt, ws)],
+                                K, warmup, stream)
+        alg = inp.num_rows * inp.max_len * 4 + inp.num_rows * inp.k * 4
+        ach = alg / (t_topk * 1e-3) / 1e9
+        log(f"{name}: {ms * 1e3:.1f} us/step (top-k {t_topk * 1e3:.1f} us)")
+        return {"_inp": inp, "rows_per_s": round(inp.num_rows / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+                "config": {"workload": name, "rows": inp.num_rows, "row_len": inp.max_len, "k": inp.k,
+                           "steps": "top-k only"},
+                "kernels_us": {"topk": round(t_topk * 1e3, 2)},
+                "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "topk (all launches)",
+                             "algorithmic_bytes": alg, "avg_us": round(t_topk * 1e3, 2)}}
+    scorer = "prefill" if name == "qsa_prefill_8k" else "decode"
+    path = IndexerPath(upload(inp, dev), scorer)
+    fns = [path.score, path.select, path.expand]
+    ms, t_score = time_steps(fns, K, warmup, stream, probe=0)
+    b_score, b_topk, b_expand = kernel_breakdown(fns, K, stream)
+    log(f"{name}: {ms * 1e3:.1f} us/step; score {t_score * 1e3:.1f} us (timed region); separate pass: "
+        f"score {b_score * 1e3:.1f} us, top-k {b_topk * 1e3:.1f} us, expand {b_expand * 1e3:.1f} us")
+    if scorer == "decode":
+        alg = scorer_bytes(inp)
+        ach = alg / (t_score * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("score_decode", source_digest("score_decode.hip", "device.h")),
+                "kernel": "score_decode_kernel", "algorithmic_bytes": alg, "avg_us": round(t_score * 1e3, 2)}
+    else:
+        fl = prefill_flops(inp)
+        ach = fl / (t_score * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic("score_prefill", source_digest("score_prefill.hip", "device.h")),
+                "kernel": "score_prefill_kernel", "algorithmic_flops": fl, "avg_us": round(t_score * 1e3, 2)}
+    return {"_inp": inp, "rows_per_s": round(inp.num_rows / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+            "config": {"workload": name, "rows": inp.num_rows, "requests": inp.num_req,
+                       "max_visible_blocks": inp.max_vis, "k": inp.k, "c": inp.c, "scorer": scorer,
+                       "page_tokens": 64},
+            "kernels_us": {"score": round(b_score * 1e3, 2), "topk": round(b_topk * 1e3, 2),
+                           "expand": round(b_expand * 1e3, 2),
+                           "note": "separate pass after the timed region, every call bracketed by HIP events"},
+            "roofline": roof}
 
 
 def main():
@@ -101,83 +223,32 @@ def main():
     ap.add_argument("--workload", default="dsa_decode_16x80k")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time every other workload (extra field)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): every call of this path runs on one "
               "GPU with no collectives; see the sharding note in DESIGN.md", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synth
-    from block_scoring_top_amd.pipeline import IndexerPath
-    from synth.device import upload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    gen = synth.WORKLOADS[args.workload]
-    log(f"generating {args.workload}")
-    inp = gen()
-    scorer = "prefill" if args.workload == "qsa_prefill_8k" else "decode"
-    dinp = upload(inp, dev)
-    path = IndexerPath(dinp, scorer)
-    log(f"rows={inp.num_rows} max_vis={inp.max_vis} k={inp.k} c={inp.c} scorer={scorer}")
-
-    for _ in range(args.warmup):
-        path.run()
-    torch.cuda.synchronize()
-    log("warmup done")
-
-    stream = torch.cuda.current_stream(dev)
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(K):
-        e = ev[i]
-        e[0].record(stream)
-        path.score()
-        e[1].record(stream)
-        path.select()
-        e[2].record(stream)
-        path.expand()
-        e[3].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / K
-    t_score = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    t_expand = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    log(f"timed {K} steps: {ms_step * 1e3:.1f} us/step (host wall {wall * 1e6 / K:.1f} us/step); "
-        f"score {t_score * 1e3:.1f} us, top-k {t_topk * 1e3:.1f} us, expand {t_expand * 1e3:.1f} us")
-
-    rows_per_s = inp.num_rows / (ms_step * 1e-3)
-    if scorer == "decode":
-        alg = scorer_bytes(inp)
-        achieved = alg / (t_score * 1e-3) / 1e9
-        kname = "score_decode"
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(kname, source_digest("score_decode.hip", "device.h")),
-                "kernel": "score_decode_kernel", "algorithmic_bytes": alg, "avg_us": round(t_score * 1e3, 2)}
-    else:
-        fl = prefill_flops(inp)
-        achieved = fl / (t_score * 1e-3) / 1e12
-        kname = "score_prefill"
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(kname, source_digest("score_prefill.hip", "device.h")),
-                "kernel": "score_prefill_kernel", "algorithmic_flops": fl, "avg_us": round(t_score * 1e3, 2)}
-
+    res = run_workload(args.workload, args.steps, args.warmup, dev)
+    inp = res.pop("_inp")
+    extra = {}
+    if args.all:
+        for name in synth.WORKLOADS:
+            if name == args.workload:
+                continue
+            r = run_workload(name, args.steps, args.warmup, dev)
+            r.pop("_inp")
+            extra[name] = r
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -185,25 +256,24 @@ def main():
 
     line = {
         "metric": "indexer rows/s (score+top-k) at L=80k; achieved HBM GB/s and % of peak",
-        "value": round(rows_per_s, 1),
+        "value": res["rows_per_s"],
         "unit": "rows/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q ~N(0,1), keys ~N(0,1) L2-normalised, bf16; random page permutation)",
-        "config": {"workload": args.workload, "rows": inp.num_rows, "requests": inp.num_req,
-                   "max_visible_blocks": inp.max_vis, "k": inp.k, "c": inp.c, "scorer": scorer,
-                   "page_tokens": 64},
-        "kernels_us": {"score": round(t_score * 1e3, 2), "topk": round(t_topk * 1e3, 2),
-                       "expand": round(t_expand * 1e3, 2)},
-        "roofline": roof,
+        "config": res["config"],
+        "kernels_us": res["kernels_us"],
+        "roofline": res["roofline"],
         "cpu_baseline": cpu,
     }
+    if extra:
+        line["other_workloads"] = extra
     print(json.dumps(line), flush=True)
 
 

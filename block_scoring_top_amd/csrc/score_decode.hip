@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   const int b = blockIdx.y;
   const int r0 = req_row_ptr[b];
   const int r1 = req_row_ptr[b + 1];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
 
   int nmax = 0;
   for (int r = r0; r < r1; ++r) nmax = max(nmax, (row_pos[r] + 1) / c);
@@ -76,7 +76,23 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   const int per_page = kPage / c;
   const int sub = tid & 15;  // 16-byte slice: dims 8*sub .. 8*sub+7
   const int kin = tid >> 4;  // key within a 16-key round
+  // The chunk spans at most 64 pages (host sizing): lane i of every wave
+  // holds the chunk's i-th page id, read back with v_readlane per round.
   const int32_t* pt = page_table + (int64_t)b * pt_stride;
+  const int first_page = (c * j0) >> 6;
+  const int npages = ((c * (j1 - 1)) >> 6) - first_page + 1;
+  const int32_t my_page = lane < npages ? pt[first_page + lane] : -1;
+
+  auto round_slot = [&](int jb, bool& ok) -> int64_t {
+    // Keys past the chunk are clamped onto its last key (always a valid
+    // read); their scores are never stored.  A 16-aligned round lies in one
+    // page, so the page id is uniform.
+    const int jc = min(jb, j1 - 1);
+    const int page = __builtin_amdgcn_readlane(my_page, ((c * jc) >> 6) - first_page);
+    ok = page >= 0 && page < num_pages;
+    const int j = min(jb + kin, j1 - 1);
+    return ok ? (int64_t)page * per_page + (j & (per_page - 1)) : 0;
+  };
 
   for (int g0 = r0; g0 < r1; g0 += RG) {
     const int ng = min(RG, r1 - g0);
@@ -84,46 +100,42 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
     int nvis[RG];
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
-      if (i < ng) {
-        const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(q + (int64_t)(g0 + i) * kHeads * kDim) + sub;
+      const int r = g0 + min(i, ng - 1);
+      const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(q + (int64_t)r * kHeads * kDim) + sub;
 #pragma unroll
-        for (int h = 0; h < kHeads; ++h) qv[i][h] = qp[h * (kDim / 8)];
-        nvis[i] = min((row_pos[g0 + i] + 1) / c, max_vis);
-      } else {
-#pragma unroll
-        for (int h = 0; h < kHeads; ++h) qv[i][h] = u32x4_t{0u, 0u, 0u, 0u};
-        nvis[i] = 0;
-      }
+      for (int h = 0; h < kHeads; ++h) qv[i][h] = qp[h * (kDim / 8)];
+      nvis[i] = i < ng ? min((row_pos[r] + 1) / c, max_vis) : 0;
     }
 
-    for (int jr = j0; jr < j1; jr += 16 * U) {
-      u32x4_t kv[U];
-      bool ok[U];
+    u32x4_t kv[U];
+    bool ok[U];
+    auto issue = [&](int jr) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int jb = jr + 16 * u;  // 16-aligned: the round lies in one page
-        const int j = jb + kin;
-        kv[u] = u32x4_t{0u, 0u, 0u, 0u};
-        ok[u] = true;
-        if (jb < j1) {
-          const int32_t page = pt[(c * jb) >> 6];
-          ok[u] = page >= 0 && page < num_pages;
-          if (ok[u] && j < j1) {
-            const int64_t slot = (int64_t)page * per_page + (j & (per_page - 1));
-            kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kcache + slot * kDim) + sub);
-          }
-        }
+        const int64_t slot = round_slot(jr + 16 * u, ok[u]);
+        kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kcache + slot * kDim) + sub);
       }
+    };
+    issue(j0);
+    for (int jr = j0; jr < j1; jr += 16 * U) {
+      u32x4_t cur[U];
+      bool cok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        cur[u] = kv[u];
+        cok[u] = ok[u];
+      }
+      if (jr + 16 * U < j1) issue(jr + 16 * U);  // next group in flight during this one
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = jr + 16 * u + kin;
 #pragma unroll
         for (int i = 0; i < RG; ++i) {
           if (i < ng) {
-            const float s = row_head_relu_sum(slice_dot(kv[u], qv[i][0]), slice_dot(kv[u], qv[i][1]),
-                                              slice_dot(kv[u], qv[i][2]), slice_dot(kv[u], qv[i][3]), sub);
+            const float sc = row_head_relu_sum(slice_dot(cur[u], qv[i][0]), slice_dot(cur[u], qv[i][1]),
+                                               slice_dot(cur[u], qv[i][2]), slice_dot(cur[u], qv[i][3]), sub);
             if (sub == 0 && j < j1 && j < nvis[i])
-              scores[(int64_t)(g0 + i) * ld + j] = ok[u] ? s * kScale : __builtin_nanf("");
+              scores[(int64_t)(g0 + i) * ld + j] = cok[u] ? sc * kScale : __builtin_nanf("");
           }
         }
       }
@@ -143,11 +155,14 @@ int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_p
                         int32_t c, int32_t max_vis,
                         float* scores, int64_t ld, int32_t* row_len, hipStream_t stream) {
   constexpr int U = 4;
-  // Chunk: a multiple of one unrolled round (64 keys), sized so a launch has
-  // a few thousand workgroups when the batch is large.
+  // Chunk: a multiple of one unrolled group (16*U keys), at most 64 pages
+  // (1,024 keys for c = 4, 4,096 for c = 1), sized so a large batch gets a
+  // few thousand workgroups.
+  const int64_t group = 16 * U;
+  const int64_t max_chunk = 64 * (kPage / c);
   const int64_t keys = (int64_t)max_vis * num_req;
-  int64_t chunk = (keys / 2048 + 63) / 64 * 64;
-  chunk = chunk < 64 ? 64 : (chunk > 4096 ? 4096 : chunk);
+  int64_t chunk = (keys / 2048 + group - 1) / group * group;
+  chunk = chunk < group ? group : (chunk > max_chunk ? max_chunk : chunk);
   const int nchunks = max_vis > 0 ? (int)((max_vis + chunk - 1) / chunk) : 1;
   dim3 grid(nchunks, num_req), block(256);
   const int rg = pick_rg(num_rows, num_req);
