@@ -1,7 +1,9 @@
 """Benchmark of the indexer hot path on one MI355X.
 
 A step is one pass of the whole path over one batch already resident in HBM:
-score (decode scorer) -> top-k -> expand/translate.  The default workload is
+score (decode scorer) -> top-k -> expand/translate, the last two fused in one
+kernel (idx_select_translate; --unfused times the separate calls).  The
+default workload is
 the uncompressed (c = 1) DSA-style decode: 16 requests x 1 row at L = 81,920
 tokens, an independent 81,920 x 128 bf16 key set per request (320 MiB),
 top-2048, translation through 64-token pages.
@@ -154,7 +156,7 @@ def kernel_breakdown(fns, K, stream):
     return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(len(fns))]
 
 
-def run_workload(name, K, warmup, dev):
+def run_workload(name, K, warmup, dev, fused=True):
     import torch
 
     import block_scoring_top_amd as bst
@@ -186,11 +188,14 @@ def run_workload(name, K, warmup, dev):
                              "algorithmic_bytes": alg, "avg_us": round(t_topk * 1e3, 2)}}
     scorer = "prefill" if name == "qsa_prefill_8k" else "decode"
     path = IndexerPath(upload(inp, dev), scorer)
-    fns = [path.score, path.select, path.expand]
+    if fused:
+        fns, names = [path.score, path.select_translate], ["score", "select_translate"]
+    else:
+        fns, names = [path.score, path.select, path.expand], ["score", "topk", "expand"]
     ms, t_score = time_steps(fns, K, warmup, stream, probe=0)
-    b_score, b_topk, b_expand = kernel_breakdown(fns, K, stream)
-    log(f"{name}: {ms * 1e3:.1f} us/step; score {t_score * 1e3:.1f} us (timed region); separate pass: "
-        f"score {b_score * 1e3:.1f} us, top-k {b_topk * 1e3:.1f} us, expand {b_expand * 1e3:.1f} us")
+    br = kernel_breakdown(fns, K, stream)
+    log(f"{name}: {ms * 1e3:.1f} us/step; score {t_score * 1e3:.1f} us (timed region); separate pass: " +
+        ", ".join(f"{n} {t * 1e3:.1f} us" for n, t in zip(names, br)))
     if scorer == "decode":
         alg = scorer_bytes(inp)
         ach = alg / (t_score * 1e-3) / 1e9
@@ -208,9 +213,10 @@ def run_workload(name, K, warmup, dev):
     return {"_inp": inp, "rows_per_s": round(inp.num_rows / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
             "config": {"workload": name, "rows": inp.num_rows, "requests": inp.num_req,
                        "max_visible_blocks": inp.max_vis, "k": inp.k, "c": inp.c, "scorer": scorer,
-                       "page_tokens": 64},
-            "kernels_us": {"score": round(b_score * 1e3, 2), "topk": round(b_topk * 1e3, 2),
-                           "expand": round(b_expand * 1e3, 2),
+                       "page_tokens": 64,
+                       "steps": "score -> select+translate (one kernel)" if fused else
+                                "score -> top-k -> expand/translate"},
+            "kernels_us": {**{n: round(t * 1e3, 2) for n, t in zip(names, br)},
                            "note": "separate pass after the timed region, every call bracketed by HIP events"},
             "roofline": roof}
 
@@ -224,6 +230,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every other workload (extra field)")
+    ap.add_argument("--unfused", action="store_true", help="separate top-k and expand calls")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): every call of this path runs on one "
@@ -239,14 +246,14 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    res = run_workload(args.workload, args.steps, args.warmup, dev)
+    res = run_workload(args.workload, args.steps, args.warmup, dev, fused=not args.unfused)
     inp = res.pop("_inp")
     extra = {}
     if args.all:
         for name in synth.WORKLOADS:
             if name == args.workload:
                 continue
-            r = run_workload(name, args.steps, args.warmup, dev)
+            r = run_workload(name, args.steps, args.warmup, dev, fused=not args.unfused)
             r.pop("_inp")
             extra[name] = r
     cpu = None

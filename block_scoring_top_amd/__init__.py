@@ -54,6 +54,9 @@ def lib():
         L.topk_select_rows.restype = C.c_int
         L.idx_expand_translate.argtypes = [P, P, i32, P, i32, P, i32, i32, P, i32, P, P, P, i32, P]
         L.idx_expand_translate.restype = C.c_int
+        L.idx_select_translate.argtypes = [P, i64, P, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P, P, i32,
+                                           P, C.c_size_t, P]
+        L.idx_select_translate.restype = C.c_int
         L.bs_status_string.argtypes = [C.c_int]
         L.bs_status_string.restype = C.c_char_p
         L.bs_abi_version.argtypes = []
@@ -182,7 +185,33 @@ def idx_expand_translate(sel, sel_count, k, req_row_ptr, row_pos, c, page_table,
     _check(st, "idx_expand_translate")
 
 
+def idx_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                         out_slots, out_count, out_pos=None, workspace=None, stream=None):
+    """Top-k and expand/translate in one kernel.  See ``idx_select_translate`` in blockscore.h."""
+    dev = scores.device
+    R = int(scores.shape[0])
+    if sel.dim() != 2 or sel.shape[0] != R or sel.shape[1] != k:
+        raise ValueError("sel must be [num_rows, k]")
+    if sel_count.numel() != R or row_len.numel() != R or row_pos.numel() != R:
+        raise ValueError("row_len, row_pos and sel_count must hold num_rows entries")
+    if out_slots.dim() != 2 or out_slots.shape[0] != R:
+        raise ValueError("out_slots must be [num_rows, ld_out]")
+    if out_pos is not None and out_pos.shape != out_slots.shape:
+        raise ValueError("out_pos must match out_slots")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().idx_select_translate(
+        _ptr(scores, _F32, "scores", dev), int(scores.stride(0)), _ptr(row_len, _I32, "row_len", dev), R,
+        int(max_len), int(k), _ptr(req_row_ptr, _I32, "req_row_ptr", dev), int(req_row_ptr.shape[0]) - 1,
+        _ptr(row_pos, _I32, "row_pos", dev), int(c), _ptr(page_table, _I32, "page_table", dev),
+        int(page_table.shape[1]), _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev),
+        _ptr(out_slots, _I32, "out_slots", dev), _ptr(out_pos, _I32, "out_pos", dev),
+        _ptr(out_count, _I32, "out_count", dev), int(out_slots.stride(0)),
+        _ptr(workspace, (torch.uint8,), "workspace", dev), ws_bytes, _stream(stream, dev))
+    _check(st, "idx_select_translate")
+
+
 __all__ = [
     "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
-    "topk_select_rows", "idx_expand_translate", "status_string", "BlockScoreError", "lib",
+    "topk_select_rows", "idx_expand_translate", "idx_select_translate", "status_string", "BlockScoreError",
+    "lib",
 ]

@@ -92,6 +92,30 @@ BS_EXPORT int idx_expand_translate(const int32_t* sel, const int32_t* sel_count,
                            out_slots, out_pos, out_count, ld_out, static_cast<hipStream_t>(stream));
 }
 
+BS_EXPORT int idx_select_translate(const float* scores, int64_t ld_scores, const int32_t* row_len,
+                                   int32_t num_rows, int32_t max_len, int32_t k,
+                                   const int32_t* req_row_ptr, int32_t num_req, const int32_t* row_pos, int32_t c,
+                                   const int32_t* page_table, int32_t pt_stride,
+                                   int32_t* sel, int32_t* sel_count,
+                                   int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_rows < 0 || num_req < 0 || max_len < 0 || k < 1 || k > BS_KMAX) return BS_ERR_ARG;
+  if (c != 1 && c != 4) return BS_ERR_ARG;
+  if ((int64_t)ld_out < (int64_t)k * c + c - 1) return BS_ERR_ARG;
+  if (num_rows == 0) return BS_OK;
+  if (num_req == 0) return BS_ERR_ARG;
+  if (!scores || !row_len || !sel || !sel_count || !req_row_ptr || !row_pos || !page_table || !out_slots ||
+      !out_count)
+    return BS_ERR_NULL;
+  if (ld_scores < (int64_t)max_len || pt_stride < 1) return BS_ERR_ARG;
+  if ((int64_t)max_len > (int64_t)65535 * 4096) return BS_ERR_ARG;  // grid y limit
+  const size_t need = bs::topk_workspace_size(num_rows, max_len, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return BS_ERR_WORKSPACE;
+  return bs::launch_select_translate(scores, ld_scores, row_len, num_rows, max_len, k, req_row_ptr, num_req,
+                                     row_pos, c, page_table, pt_stride, sel, sel_count, out_slots, out_pos,
+                                     out_count, ld_out, workspace, static_cast<hipStream_t>(stream));
+}
+
 BS_EXPORT const char* bs_status_string(int status) {
   switch (status) {
     case BS_OK: return "BS_OK";

@@ -46,6 +46,58 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// Integer DPP move: lanes whose source is outside the row (bound_ctrl) or
+// whose row is masked out read 0.
+enum : int {
+  kDppRowShr1 = 0x111,
+  kDppRowShr2 = 0x112,
+  kDppRowShr4 = 0x114,
+  kDppRowShr8 = 0x118,
+  kDppRowBcast15 = 0x142,  // lane 15 of each row -> the next row
+  kDppRowBcast31 = 0x143   // lane 31 -> rows 2 and 3
+};
+
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND = true>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, BOUND);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active):
+// Hillis-Steele within each 16-lane row, then the row carries.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<kDppRowShr1>(x);
+  x += dpp_u32<kDppRowShr2>(x);
+  x += dpp_u32<kDppRowShr4>(x);
+  x += dpp_u32<kDppRowShr8>(x);
+  x += dpp_u32<kDppRowBcast15, 0xA, false>(x);
+  x += dpp_u32<kDppRowBcast31, 0xC, false>(x);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t readlane(uint32_t x, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
+// Bitwise AND / OR of a 64-bit value over the wave, in every lane: the four
+// DPP row permutations reach all 16 lanes of a row, readlane joins the rows.
+template <bool AND>
+__device__ __forceinline__ uint32_t wave_bits32(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return AND ? (a & b) : (a | b); };
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppQuadXor2, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowHalfMirror, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowMirror, 0xF, 0xF, false));
+  return op(op(readlane(x, 0), readlane(x, 16)), op(readlane(x, 32), readlane(x, 48)));
+}
+
+__device__ __forceinline__ uint64_t wave_and64(uint64_t x) {
+  return ((uint64_t)wave_bits32<true>((uint32_t)(x >> 32)) << 32) | wave_bits32<true>((uint32_t)x);
+}
+
+__device__ __forceinline__ uint64_t wave_or64(uint64_t x) {
+  return ((uint64_t)wave_bits32<false>((uint32_t)(x >> 32)) << 32) | wave_bits32<false>((uint32_t)x);
+}
+
 // Order-preserving keys.  -0.0 is folded to +0.0 first so that equal values
 // get equal keys; non-negative patterns get the sign bit set and negative
 // patterns are inverted, so unsigned key order equals numeric order.
@@ -67,6 +119,19 @@ __device__ __forceinline__ uint32_t bin_of(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Reads FP32 entries of one row through a raw buffer resource: one lane
+// offset per load (no 64-bit address registers), and the hardware range check
+// returns 0 for entries at or past n, so reads past the row never fault.
+struct RowReader {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ RowReader(const float* row, int n)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0, n > 0 ? n * 4 : 0,
+                                               0x00020000)) {}
+  __device__ __forceinline__ float operator[](int idx) const {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, idx * 4, 0, 0));
+  }
+};
 
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {

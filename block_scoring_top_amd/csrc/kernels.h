@@ -27,6 +27,12 @@ int launch_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t
                 int32_t max_len, int32_t k, int32_t* sel, int32_t* sel_count,
                 void* workspace, hipStream_t stream);
 
+int launch_select_translate(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows,
+                            int32_t max_len, int32_t k, const int32_t* req_row_ptr, int32_t num_req,
+                            const int32_t* row_pos, int32_t c, const int32_t* page_table, int32_t pt_stride,
+                            int32_t* sel, int32_t* sel_count, int32_t* out_slots, int32_t* out_pos,
+                            int32_t* out_count, int32_t ld_out, void* workspace, hipStream_t stream);
+
 int launch_expand(const int32_t* sel, const int32_t* sel_count, int32_t k,
                   const int32_t* req_row_ptr, int32_t num_req,
                   const int32_t* row_pos, int32_t num_rows, int32_t c,

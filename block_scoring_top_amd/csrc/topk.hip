@@ -1,4 +1,5 @@
-// topk.hip - exact top-k per FP32 score row, as a selection rather than a sort.
+// topk.hip - exact top-k per FP32 score row, as a selection rather than a sort,
+// optionally fused with expand / append / page translation.
 //
 // Follows the TopK-V2 description (GLM-5.2 on SGLang blog, Kernel Optimization
 // > TopK-V2, text and Figures 2-3): each FP32 score is rounded to FP16 and
@@ -8,68 +9,104 @@
 // exactly.  The page leaves the exact tie rule open; here equal scores go to
 // the lower index, so the boundary is resolved by radix selection on the
 // 64-bit pair (FP32 key, inverted index), which makes every key unique and the
-// result exactly m entries.
+// result exactly m entries.  The same blog fuses the selection with the
+// page-table transform; the TRANSLATE kernels do that (expand each chosen
+// block to its token positions, append the pending tokens, translate to
+// physical slots, as the QSA section of the Qwen3.8-Flash-Next SGLang page
+// describes).
 //
-// CDNA4 has no thread-block clusters or distributed shared memory, so the
-// blog's 8-CTA cluster becomes:
-//   * rows up to 16,384 entries: one 1,024-lane workgroup keeps the row in
-//     registers (16 per lane) between the histogram and emission passes;
-//   * rows up to 32,768 entries: one workgroup streams the row twice;
-//   * longer rows: one workgroup per 4,096-entry chunk.  Each builds an LDS
-//     histogram and merges it into the row's global histogram with
-//     device-scope atomics (first launch).  In the second launch every
-//     chunk's workgroup reads the merged histogram, finds the threshold bin,
-//     emits its own above-threshold entries through a global atomic cursor and
-//     appends its boundary candidates to a workspace list.  A third launch
-//     (one workgroup per row) resolves the boundary bin and restores the
-//     row's workspace to zero.  The hand-offs sit at kernel boundaries: an
-//     in-kernel device-scope fence on gfx950 writes back and invalidates the
-//     per-XCD L2, which costs far more than a launch; and no workgroup ever
-//     waits on another, so co-residency is never assumed.
+// CDNA4 has no thread-block clusters or distributed shared memory.  The
+// blog's paths become:
+//   * many rows (a batch that fills the chip): one 1,024-lane workgroup per
+//     row, the row held in registers (16 values per lane, up to 16,384
+//     entries), longer rows streamed twice;
+//   * few long rows (>= 32,769 entries, at most 256 rows): one 256-lane
+//     workgroup per 4,096-entry chunk (16 entries per lane, in registers).
+//     A first launch merges the chunks' LDS histograms into the row's
+//     histogram with device atomics.  In a second launch every chunk finds
+//     the threshold bin, emits and translates its own above-threshold entries
+//     and appends its boundary-bin entries to the row's candidate list; the
+//     last chunk to arrive (a device-scope counter) resolves the boundary bin
+//     from that list.  No workgroup waits on another (no co-residency
+//     assumption) and no device-scope fence is issued: on gfx950 such a fence
+//     writes back and invalidates the per-XCD L2, which measured far costlier
+//     than the whole kernel.  Data crossing workgroups inside a launch (the
+//     candidate list, the counters) moves only through device-scope atomic
+//     loads and stores, performed at the device coherence point; each chunk
+//     waits for its stores to complete before it arrives;
+//   * emission is count, block scan, write (no per-entry atomics); the
+//     threshold scans and the boundary refinement run on one wave,
+//     wave-synchronously, with DPP scans (no block barriers inside).
 #include "device.h"
 #include "kernels.h"
 
 namespace bs {
 
-constexpr int kTkBlock = 1024;
-constexpr int kTkWaves = kTkBlock / 64;
-constexpr int kTkVpt = 16;                         // register path: values per lane
-constexpr int kTkShortMax = kTkBlock * kTkVpt;     // 16,384
-constexpr int kTkLongMin = 32769;                  // rows this long use several workgroups
-constexpr int kTkChunk = 4096;                     // entries per workgroup on long rows
-static_assert(kTkChunk % kTkBlock == 0, "a long-row chunk is a whole number of passes");
-constexpr int kTkCand = 4096;                      // boundary candidates kept in LDS / workspace
+constexpr int kRowNT = 1024;                   // lanes per workgroup, one row per workgroup
+constexpr int kRowVpt = 16;                    // register path: values per lane
+constexpr int kRowCand = 2048;                 // boundary candidates held in LDS (row kernel)
+constexpr int kLongNT = 256;                   // lanes per workgroup on the long-row kernels
+constexpr int kLongVpt = 16;                   // values per lane held at once there
+constexpr int kLongCand = 4096;
+constexpr int kLongMin = 32769;                // rows this long use several workgroups...
+constexpr int kLongRowsMax = 256;              // ...when the batch has at most this many rows
+constexpr int kChunk = 4096;                   // entries per workgroup on long rows
+constexpr int kPerLane = kChunk / kLongNT;     // 16
+static_assert(kChunk % kLongNT == 0, "a long-row chunk is a whole number of lanes");
+static_assert(4 * kChunk / kPage <= kLongNT, "a chunk's logical pages fit one per lane");
 
-// Workspace record per row (long rows only): merged histogram, counters,
-// candidate list.
+// Workspace record per row (long rows only): merged histogram, counters
+// ([0] arrivals, [1] emitted above the threshold, [2] boundary candidates),
+// boundary candidate list.
 constexpr size_t kWsHist = 0;
-constexpr size_t kWsCtr = kBins * 4;  // [0] emit cursor, [1] candidates, [2] threshold bin, [3] count above it
+constexpr size_t kWsCtr = kBins * 4;
 constexpr size_t kWsCand = kWsCtr + 64;
-constexpr size_t kWsRow = kWsCand + (size_t)kTkCand * 8;
+constexpr size_t kWsRow = kWsCand + (size_t)kLongCand * 8;
 
+template <int CAP>
 struct TopkShared {
   uint32_t hist[kBins];
-  uint32_t hist_digit[256];
-  uint64_t cand[kTkCand];
-  uint32_t wave_sum[kTkWaves];
-  uint64_t kmin, kmax;
+  uint32_t digit[256];
+  uint64_t cand[CAP];
+  int32_t chosen[kKmax];  // the row's selection, for the fused translation
+  uint32_t wave_tot[16];
   uint32_t emit;
-  uint32_t ncand;
   uint32_t T;
   uint32_t above;
+  uint32_t last;
   uint32_t base_up, base_cand;
+  uint64_t red_and[16], red_or[16];
+  int32_t pages[256];  // page ids of a long-row chunk's token range (fused translation)
 };
 
+// Translation context (fused kernels only).
+struct Translate {
+  const int32_t* req_row_ptr;
+  int32_t num_req;
+  const int32_t* row_pos;
+  int32_t c;
+  const int32_t* page_table;
+  int32_t pt_stride;
+  int32_t* out_slots;
+  int32_t* out_pos;
+  int32_t* out_count;
+  int32_t ld_out;
+};
+
+// The inverted index is formed by one opaque v_not_b32 at the point of use:
+// left to itself the optimiser hoists it for every unrolled entry of a tile
+// (64 live registers) and spills.
+__device__ __forceinline__ uint32_t inverted_index(int idx) {
+  uint32_t r;
+  asm volatile("v_not_b32 %0, %1" : "=v"(r) : "v"(idx));
+  return r;
+}
+
 __device__ __forceinline__ uint64_t composite_key(float v, int idx) {
-  return ((uint64_t)key32_of(v) << 32) | (uint32_t)(~(uint32_t)idx);
+  return ((uint64_t)key32_of(v) << 32) | inverted_index(idx);
 }
 
 __device__ __forceinline__ int index_of(uint64_t key) { return (int)(~(uint32_t)key); }
-
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)x, m), hi = __shfl_xor((uint32_t)(x >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
 
 // Reserves a slot per lane with `p` set, one atomic per wave.  All 64 lanes
 // must call.  Returns the slot for lanes with `p` (undefined otherwise).
@@ -79,355 +116,723 @@ __device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, bool p) {
   uint32_t base = 0;
   if (n != 0) {
     if (lane_id() == 0) base = atomicAdd(counter, n);
-    base = __shfl(base, 0);
+    base = readlane(base, 0);
   }
   return base + lanes_below(mask);
 }
 
-// Largest bin T of h[0..nb) (nb <= kTkBlock) whose suffix count reaches m,
-// and the count strictly above it; m must be in [1, sum h].  Results in
-// s.T / s.above.  All lanes must call.
-__device__ void find_threshold(const uint32_t* h, int nb, uint32_t m, TopkShared& s) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) {  // only kept if no bin qualifies (m above the total: misuse)
-    s.T = 0;
-    s.above = 0;
-  }
-  const int bin = nb - 1 - tid;  // reversed: a prefix over lanes is a suffix over bins
-  const uint32_t v = tid < nb ? h[bin] : 0u;
-  uint32_t x = v;
+// One wave: over the NB counts h[0..NB) (NB a power of two <= 1024), the
+// largest bin T whose suffix count reaches m, and the count strictly above
+// T.  Lane L owns the L-th group of NB/64 bins from the top.  Returns T = 0,
+// above = 0 if no bin qualifies (m above the total: a misuse).
+template <int NB>
+__device__ __forceinline__ void wave_threshold(const uint32_t* h, uint32_t m, uint32_t& T, uint32_t& above) {
+  constexpr int PER = NB >= 64 ? NB / 64 : 1;
+  const int lane = lane_id();
+  const int top = NB - lane * PER;  // this lane's bins: top-PER .. top-1
+  uint32_t c[PER];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
+  for (int i = 0; i < PER; ++i) c[i] = top - 1 - i >= 0 ? h[top - 1 - i] : 0u;
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) t += c[i];
+  const uint32_t incl = wave_incl_scan(t);
+  const uint32_t excl = incl - t;
+  const bool mine = top > 0 && excl < m && incl >= m;
+  const uint64_t owners = __ballot(mine);
+  uint32_t bt = 0, ba = 0, acc = excl;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool hit = !found && acc + c[i] >= m;
+    bt = hit ? (uint32_t)(top - 1 - i) : bt;
+    ba = hit ? acc : ba;
+    found = found || hit;
+    acc += c[i];
   }
-  if (lane == 63) s.wave_sum[wave] = x;
-  __syncthreads();
-  uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += s.wave_sum[w];
-  x += off;
-  if (tid < nb && x >= m && x - v < m) {
-    s.T = (uint32_t)bin;
-    s.above = x - v;
-  }
-  __syncthreads();
+  const int owner = owners ? (int)__ffsll((unsigned long long)owners) - 1 : 0;
+  T = owners ? readlane(bt, owner) : 0u;
+  above = owners ? readlane(ba, owner) : 0u;
 }
 
-// Resolves the boundary bin: among the candidates (FROM_ROW: entries of the
-// row in bin T, re-read from memory; else s.cand[0..nc)), emits the `need`
-// largest composite keys through s.emit into out[].  All lanes must call.
-template <bool FROM_ROW>
-__device__ void refine(TopkShared& s, const float* __restrict__ row, int n, uint32_t T, uint32_t nc,
-                       uint32_t need, int32_t* __restrict__ out, int limit) {
-  const int tid = threadIdx.x;
-  auto for_each = [&](auto&& f) {
-    if (FROM_ROW) {
-      for (int i = tid; i < n; i += kTkBlock) {
-        const float v = row[i];
-        if (bin_of(v) == T) f(composite_key(v, i));
-      }
-    } else {
-      for (int i = tid; i < (int)nc; i += kTkBlock) f(s.cand[i]);
-    }
-  };
-  if (!FROM_ROW && need == nc) {
-    const uint32_t base = s.emit;
-    for (int i = tid; i < (int)nc; i += kTkBlock)
-      if (base + i < (uint32_t)limit) out[base + i] = index_of(s.cand[i]);
-    __syncthreads();
-    return;
-  }
-  // The common leading bits of all candidates need no pass.
-  uint64_t lo = ~0ull, hi = 0ull;
-  for_each([&](uint64_t key) {
-    lo = key < lo ? key : lo;
-    hi = key > hi ? key : hi;
-  });
+// Block-wide exclusive prefix sum of one value per lane (all lanes call);
+// `total` gets the block's sum.  Two barriers.
+template <int NT, int CAP>
+__device__ __forceinline__ uint32_t block_excl_scan(TopkShared<CAP>& s, uint32_t x, uint32_t& total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(x);
+  if (lane == 63) s.wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t a = shfl_xor64(lo, d), b = shfl_xor64(hi, d);
-    lo = a < lo ? a : lo;
-    hi = b > hi ? b : hi;
-  }
-  if (tid == 0) {
-    s.kmin = ~0ull;
-    s.kmax = 0ull;
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t t = s.wave_tot[w];
+    off += w < wave ? t : 0u;
+    tot += t;
   }
   __syncthreads();
-  if ((tid & 63) == 0) {
-    atomicMin(reinterpret_cast<unsigned long long*>(&s.kmin), (unsigned long long)lo);
-    atomicMax(reinterpret_cast<unsigned long long*>(&s.kmax), (unsigned long long)hi);
+  total = tot;
+  return off + incl - x;
+}
+
+// The whole workgroup resolves the boundary bin from s.cand[0..nc) (nc > need
+// >= 1, nc <= CAP): each lane holds up to CAP/NT candidates in registers;
+// per 8-bit digit (after the bits all candidates share) every lane adds its
+// matching candidates to an LDS digit histogram, wave 0 finds the digit, all
+// lanes narrow the prefix.  The `need` winners are emitted by count, block
+// scan, write at out[base ...] (and chosen[base ...]).
+template <int NT, int CAP, int PER>
+__device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc, uint32_t need,
+                                                 int32_t* __restrict__ out, int32_t* chosen, uint32_t base, int limit) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint64_t key[PER];
+  uint64_t a = ~0ull, o = 0ull;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t j = (uint32_t)(i * NT + tid);
+    key[i] = j < nc ? s.cand[j] : 0ull;
+    if (j < nc) {
+      a &= key[i];
+      o |= key[i];
+    }
+  }
+  a = wave_and64(a);
+  o = wave_or64(o);
+  if (lane_id() == 0) {
+    s.red_and[wave] = a;
+    s.red_or[wave] = o;
   }
   __syncthreads();
-  const uint64_t kmin = s.kmin, kmax = s.kmax;
-  // highest differing bit (kmax != kmin whenever need < nc; 0 otherwise, a misuse)
-  int hb = kmax != kmin ? 63 - __clzll((long long)(kmax ^ kmin)) : 0;
+  a = ~0ull;
+  o = 0ull;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    a &= s.red_and[w];
+    o |= s.red_or[w];
+  }
+  const uint64_t diff = a ^ o;
+  int hb = diff ? 63 - __clzll((long long)diff) : 0;
   uint64_t mask = ~((2ull << hb) - 1ull);
-  uint64_t prefix = kmax & mask;
+  uint64_t prefix = o & mask;
   uint32_t remaining = need;
   for (;;) {
     const int width = hb + 1 < 8 ? hb + 1 : 8;
     const int shift = hb + 1 - width;
     const int nb = 1 << width;
-    for (int i = tid; i < nb; i += kTkBlock) s.hist_digit[i] = 0;
+    for (int i = tid; i < 256; i += NT) s.digit[i] = 0;  // bins past nb stay 0
     __syncthreads();
-    for_each([&](uint64_t key) {
-      if ((key & mask) == prefix) atomicAdd(&s.hist_digit[(key >> shift) & (uint64_t)(nb - 1)], 1u);
-    });
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if ((uint32_t)(i * NT + tid) < nc && (key[i] & mask) == prefix)
+        atomicAdd(&s.digit[(key[i] >> shift) & (uint64_t)(nb - 1)], 1u);
     __syncthreads();
-    find_threshold(s.hist_digit, nb, remaining, s);
+    if (wave == 0) {
+      uint32_t d, ab;
+      wave_threshold<256>(s.digit, remaining, d, ab);
+      if (lane_id() == 0) {
+        s.T = d;
+        s.above = ab;
+      }
+    }
+    __syncthreads();
     const uint32_t d = s.T;
     remaining -= s.above;
     prefix |= (uint64_t)d << shift;
     mask |= (uint64_t)(nb - 1) << shift;
-    const bool settled = s.hist_digit[d] == remaining;
+    const bool settled = s.digit[d] == remaining;
     __syncthreads();
     if (settled || shift == 0) break;
     hb = shift - 1;
   }
-  // Emit every candidate whose leading bits (under mask) are >= prefix:
-  // exactly `need` of them.
-  if (FROM_ROW) {
-    for (int base = 0; base < n; base += kTkBlock) {
-      const int i = base + tid;
-      bool p = false;
-      if (i < n) {
-        const float v = row[i];
-        p = bin_of(v) == T && (composite_key(v, i) & mask) >= prefix;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) cnt += ((uint32_t)(i * NT + tid) < nc && (key[i] & mask) >= prefix) ? 1u : 0u;
+  uint32_t total;
+  uint32_t pos = base + block_excl_scan<NT>(s, cnt, total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if ((uint32_t)(i * NT + tid) < nc && (key[i] & mask) >= prefix) {
+      if (pos < (uint32_t)limit) {
+        const int idx = index_of(key[i]);
+        out[pos] = idx;
+        if (chosen) chosen[pos] = idx;
       }
-      const uint32_t pos = wave_reserve(&s.emit, p);
-      if (p && pos < (uint32_t)limit) out[pos] = i;
+      ++pos;
     }
-  } else {
-    for (int base = 0; base < (int)nc; base += kTkBlock) {
-      const int i = base + tid;
-      const bool p = i < (int)nc && (s.cand[i] & mask) >= prefix;
-      const uint32_t pos = wave_reserve(&s.emit, p);
-      if (p && pos < (uint32_t)limit) out[pos] = index_of(s.cand[i]);
+  }
+}
+
+// Holds just as many candidates per lane as nc needs.
+template <int NT, int CAP>
+__device__ __forceinline__ void block_refine(TopkShared<CAP>& s, uint32_t nc, uint32_t need, int32_t* __restrict__ out,
+                                             int32_t* chosen, uint32_t base, int limit) {
+  constexpr int PMAX = (CAP + NT - 1) / NT;
+  if (PMAX > 2 && nc <= 2u * NT) block_refine_per<NT, CAP, 2>(s, nc, need, out, chosen, base, limit);
+  else if (PMAX > 4 && nc <= 4u * NT) block_refine_per<NT, CAP, 4>(s, nc, need, out, chosen, base, limit);
+  else block_refine_per<NT, CAP, PMAX>(s, nc, need, out, chosen, base, limit);
+}
+
+// Block-wide fallback when the boundary bin overflows the LDS list: radix
+// passes re-read the row (entries in bin T), the digit histogram is built by
+// every lane, the decisions are taken by wave 0.  Rare (tie storms).
+template <int NT, int CAP>
+__device__ __forceinline__ void block_refine_from_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, uint32_t T,
+                                      uint32_t need, int32_t* __restrict__ out, int32_t* chosen, int limit) {
+  __shared__ uint64_t red_and[NT / 64], red_or[NT / 64];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint64_t a = ~0ull, o = 0ull;
+  for (int i = tid; i < n; i += NT) {
+    const float v = row[i];
+    if (bin_of(v) == T) {
+      const uint64_t key = composite_key(v, i);
+      a &= key;
+      o |= key;
+    }
+  }
+  a = wave_and64(a);
+  o = wave_or64(o);
+  if (lane_id() == 0) {
+    red_and[wave] = a;
+    red_or[wave] = o;
+  }
+  __syncthreads();
+  a = ~0ull;
+  o = 0ull;
+  for (int w = 0; w < NT / 64; ++w) {
+    a &= red_and[w];
+    o |= red_or[w];
+  }
+  const uint64_t diff = a ^ o;
+  int hb = diff ? 63 - __clzll((long long)diff) : 0;
+  uint64_t mask = ~((2ull << hb) - 1ull);
+  uint64_t prefix = o & mask;
+  uint32_t remaining = need;
+  for (;;) {
+    const int width = hb + 1 < 8 ? hb + 1 : 8;
+    const int shift = hb + 1 - width;
+    const int nb = 1 << width;
+    for (int i = tid; i < 256; i += NT) s.digit[i] = 0;  // bins past nb stay 0
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const float v = row[i];
+      if (bin_of(v) == T) {
+        const uint64_t key = composite_key(v, i);
+        if ((key & mask) == prefix) atomicAdd(&s.digit[(key >> shift) & (uint64_t)(nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t d, ab;
+      wave_threshold<256>(s.digit, remaining, d, ab);
+      if (lane_id() == 0) {
+        s.T = d;
+        s.above = ab;
+      }
+    }
+    __syncthreads();
+    const uint32_t d = s.T;
+    remaining -= s.above;
+    prefix |= (uint64_t)d << shift;
+    mask |= (uint64_t)(nb - 1) << shift;
+    const bool settled = s.digit[d] == remaining;
+    __syncthreads();
+    if (settled || shift == 0) break;
+    hb = shift - 1;
+  }
+  for (int b0 = 0; b0 < n; b0 += NT) {
+    const int i = b0 + tid;
+    bool p = false;
+    if (i < n) {
+      const float v = row[i];
+      p = bin_of(v) == T && (composite_key(v, i) & mask) >= prefix;
+    }
+    const uint32_t pos = wave_reserve(&s.emit, p);
+    if (p && pos < (uint32_t)limit) {
+      out[pos] = i;
+      if (chosen) chosen[pos] = i;
     }
   }
   __syncthreads();
 }
 
-// Appends a boundary candidate for lanes with `p`.
-__device__ __forceinline__ void push_candidate(TopkShared& s, bool p, float v, int idx) {
-  const uint32_t pos = wave_reserve(&s.ncand, p);
-  if (p && pos < (uint32_t)kTkCand) s.cand[pos] = composite_key(v, idx);
-}
-
-// One workgroup selects a whole row (n > m).  REG: the row is held in
-// registers between passes (n <= kTkShortMax).
-template <bool REG>
-__device__ void select_row(TopkShared& s, const float* __restrict__ row, int n, int m, int32_t* __restrict__ out) {
+// Emits the V values this lane holds (entry i is row[base + i*NT + lane]):
+// above-threshold indices go to out[] (and chosen[]), boundary-bin entries
+// become composite keys in s.cand.  Each lane counts its own matches, one
+// block scan of the packed counts (above << 20 | boundary) hands out the
+// positions, then plain writes: no atomics.  up_pos / cand_pos carry the
+// running totals across tiles.
+template <int NT, int V, int CAP>
+__device__ __forceinline__ void emit_tile(TopkShared<CAP>& s, const float (&x)[V], int base, int n, uint32_t T,
+                                          uint32_t& up_pos, uint32_t& cand_pos, int m, int32_t* __restrict__ out,
+                                          bool keep) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < kBins; i += kTkBlock) s.hist[i] = 0;
-  if (tid == 0) {
-    s.emit = 0;
-    s.ncand = 0;
+  uint32_t nup = 0, neq = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int idx = base + i * NT + tid;
+    const uint32_t b = bin_of(x[i]);
+    nup += (idx < n && b > T) ? 1u : 0u;
+    neq += (idx < n && b == T) ? 1u : 0u;
   }
-  __syncthreads();
-  float v[REG ? kTkVpt : 1];
-  if (REG) {
+  uint32_t total;
+  const uint32_t excl = block_excl_scan<NT>(s, (nup << 20) | neq, total);
+  uint32_t pu = up_pos + (excl >> 20), pe = cand_pos + (excl & 0xFFFFFu);
 #pragma unroll
-    for (int i = 0; i < kTkVpt; ++i) {
-      const int idx = tid + i * kTkBlock;
-      v[i] = idx < n ? row[idx] : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < kTkVpt; ++i)
-      if (tid + i * kTkBlock < n) atomicAdd(&s.hist[bin_of(v[i])], 1u);
-  } else {
-    for (int idx = tid; idx < n; idx += kTkBlock) atomicAdd(&s.hist[bin_of(row[idx])], 1u);
-  }
-  __syncthreads();
-  find_threshold(s.hist, kBins, (uint32_t)m, s);
-  const uint32_t T = s.T, above = s.above;
-  if (REG) {
-#pragma unroll
-    for (int i = 0; i < kTkVpt; ++i) {
-      const int idx = tid + i * kTkBlock;
-      const bool valid = idx < n;
-      const uint32_t b = bin_of(v[i]);
-      const bool up = valid && b > T;
-      const uint32_t pos = wave_reserve(&s.emit, up);
-      if (up && pos < (uint32_t)m) out[pos] = idx;
-      push_candidate(s, valid && b == T, v[i], idx);
-    }
-  } else {
-    for (int base = 0; base < n; base += kTkBlock) {
-      const int idx = base + tid;
-      const bool valid = idx < n;
-      const float x = valid ? row[idx] : 0.0f;
-      const uint32_t b = bin_of(x);
-      const bool up = valid && b > T;
-      const uint32_t pos = wave_reserve(&s.emit, up);
-      if (up && pos < (uint32_t)m) out[pos] = idx;
-      push_candidate(s, valid && b == T, x, idx);
+  for (int i = 0; i < V; ++i) {
+    __builtin_amdgcn_sched_barrier(0);  // keep one entry's work live at a time
+    const int idx = base + i * NT + tid;
+    if (idx < n) {
+      const uint32_t b = bin_of(x[i]);
+      if (b > T) {
+        if (pu < (uint32_t)m) {
+          out[pu] = idx;
+          if (keep) s.chosen[pu] = idx;
+        }
+        ++pu;
+      } else if (b == T) {
+        if (pe < (uint32_t)CAP) s.cand[pe] = composite_key(x[i], idx);
+        ++pe;
+      }
     }
   }
-  __syncthreads();
-  const uint32_t nc = s.ncand, need = (uint32_t)m - above;
-  if (nc <= (uint32_t)kTkCand) refine<false>(s, row, n, T, nc, need, out, m);
-  else refine<true>(s, row, n, T, nc, need, out, m);
+  up_pos += total >> 20;
+  cand_pos += total & 0xFFFFFu;
 }
 
-__device__ __forceinline__ uint8_t* ws_row(uint8_t* ws, int r) { return ws + (size_t)r * kWsRow; }
+template <int CAP>
+__device__ __forceinline__ void threshold_to_shared(TopkShared<CAP>& s, uint32_t m) {
+  if ((threadIdx.x >> 6) == 0) {
+    uint32_t T, ab;
+    wave_threshold<kBins>(s.hist, m, T, ab);
+    if (lane_id() == 0) {
+      s.T = T;
+      s.above = ab;
+    }
+  }
+  __syncthreads();
+}
 
-__global__ __launch_bounds__(kTkBlock) void topk_main_kernel(
+// One workgroup selects a whole row with n > m.  Rows of up to NT*V entries
+// are read once and held in registers; longer rows are streamed: once for
+// the histogram (skipped when it is ready), once in NT*V-entry tiles for
+// emission.  HIST_READY: s.hist
+// already holds the row's histogram (long-row finisher).  All lanes call.
+template <int NT, int V, int CAP, bool HIST_READY>
+__device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m,
+                                           int32_t* __restrict__ out, bool keep) {
+  constexpr int kTile = V;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  if (!HIST_READY)
+    for (int i = tid; i < kBins; i += NT) s.hist[i] = 0;
+  __syncthreads();
+  uint32_t up_pos = 0, cand_pos = 0;
+  uint32_t T, above;
+  const RowReader rd(row, n);
+  if (n <= NT * V) {
+    float x[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) x[i] = rd[i * NT + tid];
+    if (!HIST_READY) {
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        if (i * NT + tid < n) atomicAdd(&s.hist[bin_of(x[i])], 1u);
+    }
+    __syncthreads();
+    threshold_to_shared(s, (uint32_t)m);
+    T = s.T;
+    above = s.above;
+    emit_tile<NT, V>(s, x, 0, n, T, up_pos, cand_pos, m, out, keep);
+  } else {
+    if (!HIST_READY) {
+      for (int b0 = 0; b0 < n; b0 += NT * 8) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = rd[b0 + j * NT + tid];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (b0 + j * NT + tid < n) atomicAdd(&s.hist[bin_of(x[j])], 1u);
+      }
+    }
+    __syncthreads();
+    threshold_to_shared(s, (uint32_t)m);
+    T = s.T;
+    above = s.above;
+    for (int b0 = 0; b0 < n; b0 += NT * kTile) {
+      float x[kTile];
+#pragma unroll
+      for (int i = 0; i < kTile; ++i) x[i] = rd[b0 + i * NT + tid];
+      emit_tile<NT, kTile>(s, x, b0, n, T, up_pos, cand_pos, m, out, keep);
+    }
+  }
+  __syncthreads();
+  const uint32_t nc = cand_pos, need = (uint32_t)m - above;
+  if (need == 0 || need > (uint32_t)m) return;  // the latter only on misuse
+  int32_t* chosen = keep ? s.chosen : nullptr;
+  if (nc <= (uint32_t)CAP) {
+    if (need >= nc) {
+      for (uint32_t i = tid; i < nc; i += NT) {
+        const uint32_t at = above + i;
+        if (at < (uint32_t)m) {
+          const int idx = index_of(s.cand[i]);
+          out[at] = idx;
+          if (keep) s.chosen[at] = idx;
+        }
+      }
+    } else {
+      block_refine<NT, CAP>(s, nc, need, out, chosen, above, m);
+    }
+    __syncthreads();
+  } else {
+    if (tid == 0) s.emit = above;
+    __syncthreads();
+    block_refine_from_row<NT, CAP>(s, row, n, T, need, out, chosen, m);
+  }
+}
+
+// Request of row r: the number of request starts at or before r, minus one.
+// All 64 lanes of the calling wave must call.
+__device__ __forceinline__ int request_of(const int32_t* __restrict__ req_row_ptr, int num_req, int r) {
+  int b = -1;
+  for (int base = 0; base < num_req; base += 64) {
+    const int bi = base + lane_id();
+    const bool started = bi < num_req && req_row_ptr[bi] <= r;
+    b += __popcll(__ballot(started));
+  }
+  return max(0, min(b, num_req - 1));
+}
+
+// Fused translation.  Selection position q of row r holding block j becomes
+// output entries q*c .. q*c+c-1 (positions c*j .. c*j+c-1); after the m
+// chosen blocks come the pending positions c*n_vis .. t, then -1.  slot =
+// page_table[b][pos/64]*64 + pos mod 64 (-1 for an invalid block or page).
+struct RowGeom {
+  int b, t, nv, p;
+};
+
+__device__ __forceinline__ RowGeom row_geometry(const Translate& tr, int r) {
+  RowGeom g;
+  g.b = request_of(tr.req_row_ptr, tr.num_req, r);
+  g.t = tr.row_pos[r];
+  g.nv = g.t >= 0 ? (g.t + 1) / tr.c : 0;
+  g.p = g.t >= 0 ? g.t + 1 - tr.c * g.nv : 0;
+  return g;
+}
+
+__device__ __forceinline__ void put_slot(const Translate& tr, const RowGeom& g, int r, int i, int pos) {
+  int slot = -1;
+  if (pos >= 0 && (pos >> 6) < tr.pt_stride) {
+    const int page = tr.page_table[(int64_t)g.b * tr.pt_stride + (pos >> 6)];
+    slot = page >= 0 ? page * kPage + (pos & (kPage - 1)) : -1;
+  }
+  tr.out_slots[(int64_t)r * tr.ld_out + i] = slot;
+  if (tr.out_pos) tr.out_pos[(int64_t)r * tr.ld_out + i] = pos;
+}
+
+// Output entries of selection position q (block j).
+__device__ __forceinline__ void translate_block(const Translate& tr, const RowGeom& g, int r, int q, int j) {
+  const int c = tr.c;
+  for (int u = 0; u < c; ++u) put_slot(tr, g, r, q * c + u, (j >= 0 && j < g.nv) ? c * j + u : -1);
+}
+
+// Output entries from m*c on: the pending tail, then -1; and the count.
+template <int NT>
+__device__ __forceinline__ void translate_tail(const Translate& tr, const RowGeom& g, int r, int m) {
+  const int nblk = tr.c * m, total = nblk + g.p;
+  for (int i = nblk + (int)threadIdx.x; i < tr.ld_out; i += NT) put_slot(tr, g, r, i, i < total ? tr.c * g.nv + (i - nblk) : -1);
+  if (threadIdx.x == 0) tr.out_count[r] = total;
+}
+
+// The whole row from chosen[0..m).  All lanes call (request lookup uses
+// whole waves).
+template <int NT>
+__device__ __forceinline__ void translate_row(const Translate& tr, int r, int m, const int32_t* chosen) {
+  const RowGeom g = row_geometry(tr, r);
+  const int c = tr.c;
+  for (int i = threadIdx.x; i < c * m; i += NT) {
+    const int q = i / c, j = chosen[q];
+    put_slot(tr, g, r, i, (j >= 0 && j < g.nv) ? c * j + (i - q * c) : -1);
+  }
+  translate_tail<NT>(tr, g, r, m);
+}
+
+// The whole selection of one row by one workgroup, any n.
+template <int NT, int VPT, int CAP, bool TRANSLATE>
+__device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m, int k,
+                                 int32_t* __restrict__ out, int32_t* __restrict__ sel_count, int r,
+                                 const Translate& tr) {
+  const int tid = threadIdx.x;
+  for (int i = m + tid; i < k; i += NT) out[i] = -1;
+  if (tid == 0) sel_count[r] = m;
+  if (m == n) {
+    for (int i = tid; i < n; i += NT) {
+      out[i] = i;
+      if (TRANSLATE) s.chosen[i] = i;
+    }
+  } else {
+    select_row<NT, VPT, CAP, false>(s, row, n, m, out, TRANSLATE);
+  }
+  if (TRANSLATE) {
+    __syncthreads();
+    translate_row<NT>(tr, r, m, s.chosen);
+  }
+}
+
+// Many rows: one 256-lane workgroup per row.
+template <bool TRANSLATE>
+__global__ __launch_bounds__(kRowNT) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
-    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws) {
-  __shared__ TopkShared s;
+    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, Translate tr) {
+  __shared__ TopkShared<kRowCand> s;
+  const int r = blockIdx.x;
+  const int n = max(0, min(row_len[r], max_len));
+  const int m = min(k, n);
+  select_whole_row<kRowNT, kRowVpt, kRowCand, TRANSLATE>(s, scores + (int64_t)r * ld, n, m, k,
+                                                          sel + (int64_t)r * k, sel_count, r, tr);
+}
+
+// Output entries of selection position q (block j of a long-row chunk),
+// page ids from the chunk's LDS copy.
+template <int C>
+__device__ __forceinline__ void translate_block_lds(const Translate& tr, int r, int q, int j, const int32_t* pages,
+                                                    int first_lp) {
+  int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out + q * C;
+  int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out + q * C : nullptr;
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    const int pos = C * j + u;
+    const int page = pages[(pos >> 6) - first_lp];
+    orow[u] = page >= 0 ? page * kPage + (pos & (kPage - 1)) : -1;
+    if (prow) prow[u] = pos;
+  }
+}
+
+// Few long rows, first launch: one 256-lane workgroup per 4,096-entry chunk
+// merges its LDS histogram into the row's histogram with device atomics.
+// Rows shorter than kLongMin are done whole by their first workgroup.
+template <bool TRANSLATE>
+__global__ __launch_bounds__(kLongNT) void topk_long_hist_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
+    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
+    Translate tr) {
+  __shared__ TopkShared<kLongCand> s;
   const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x;
   const int n = max(0, min(row_len[r], max_len));
   const int m = min(k, n);
   const float* row = scores + (int64_t)r * ld;
-  int32_t* out = sel + (int64_t)r * k;
-
-  if (n >= kTkLongMin) {
-    // Long row, first launch: this chunk's histogram merged into the row's.
-    const int lo = w * kTkChunk;
-    if (lo >= n) return;
-    const int hi = min(n, lo + kTkChunk);
-    s.hist[tid] = 0;
-    __syncthreads();
-    for (int idx = lo + tid; idx < hi; idx += kTkBlock) atomicAdd(&s.hist[bin_of(row[idx])], 1u);
-    __syncthreads();
-    const uint32_t cnt = s.hist[tid];
-    if (cnt != 0) atomicAdd(reinterpret_cast<uint32_t*>(ws_row(ws, r) + kWsHist) + tid, cnt);
+  if (n < kLongMin) {
+    if (w == 0)
+      select_whole_row<kLongNT, kLongVpt, kLongCand, TRANSLATE>(s, row, n, m, k, sel + (int64_t)r * k, sel_count,
+                                                                 r, tr);
     return;
   }
-  if (w != 0) return;
-  for (int i = m + tid; i < k; i += kTkBlock) out[i] = -1;
-  if (tid == 0) sel_count[r] = m;
-  if (m == n) {
-    for (int i = tid; i < n; i += kTkBlock) out[i] = i;
-    return;
+  const int lo = w * kChunk;
+  if (lo >= n) return;
+  uint32_t* gh = reinterpret_cast<uint32_t*>(ws + (size_t)r * kWsRow + kWsHist);
+  for (int i = tid; i < kBins; i += kLongNT) s.hist[i] = 0;
+  __syncthreads();
+  const RowReader rd(row, n);
+  float x[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) x[i] = rd[lo + i * kLongNT + tid];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i)
+    if (lo + i * kLongNT + tid < n) atomicAdd(&s.hist[bin_of(x[i])], 1u);
+  __syncthreads();
+  for (int i = tid; i < kBins; i += kLongNT) {
+    const uint32_t cnt = s.hist[i];
+    if (cnt != 0) __hip_atomic_fetch_add(&gh[i], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (n <= kTkShortMax) select_row<true>(s, row, n, m, out);
-  else select_row<false>(s, row, n, m, out);
 }
 
-// Long rows, second launch: every chunk's workgroup finds the threshold bin
-// from the merged histogram, emits its above-threshold entries and appends
-// its boundary candidates to the row's workspace list.
-__global__ __launch_bounds__(kTkBlock) void topk_long_emit_kernel(
+// Few long rows, second launch.  Every chunk's workgroup reads the merged
+// histogram, finds the threshold bin, emits (and translates) its own
+// above-threshold entries through one device atomic per workgroup, and
+// appends its boundary-bin entries to the row's candidate list with
+// device-scope stores.  It waits for those stores to complete and arrives on
+// the row's counter; the last to arrive resolves the boundary bin from the
+// candidate list (read back with device-scope loads), writes the pending tail
+// and leaves the row's workspace zero-filled.  No fence, no spin.
+template <bool TRANSLATE>
+__global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
-    int32_t k, int32_t* __restrict__ sel, uint8_t* __restrict__ ws) {
-  __shared__ TopkShared s;
-  const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x;
+    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
+    Translate tr) {
+  __shared__ TopkShared<kLongCand> s;
+  const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
   const int n = max(0, min(row_len[r], max_len));
-  if (n < kTkLongMin) return;
-  if (w * kTkChunk >= n) return;
+  if (n < kLongMin) return;
+  const int lo = w * kChunk;
+  if (lo >= n) return;
+  const int nchunk = (n + kChunk - 1) / kChunk;
   const int m = k;  // n > 2048 >= k
   const float* row = scores + (int64_t)r * ld;
   int32_t* out = sel + (int64_t)r * k;
-  uint8_t* rec = ws_row(ws, r);
-  const uint32_t* gh = reinterpret_cast<const uint32_t*>(rec + kWsHist);
-  uint32_t* ctr = reinterpret_cast<uint32_t*>(rec + kWsCtr);
-  uint64_t* gcand = reinterpret_cast<uint64_t*>(rec + kWsCand);
-
-  s.hist[tid] = gh[tid];
-  if (tid == 0) {
-    s.emit = 0;
-    s.ncand = 0;
-  }
-  __syncthreads();
-  find_threshold(s.hist, kBins, (uint32_t)m, s);
-  const uint32_t T = s.T;
-  if (w == 0 && tid == 0) {
-    ctr[2] = T;
-    ctr[3] = s.above;
-  }
-  // Reserve output positions inside the workgroup first (LDS atomics), then
-  // one device-scope atomic per list for the whole workgroup: same-address
-  // device atomics serialise, so per-wave reservations would queue up.
-  const int lo = w * kTkChunk, hi = min(n, lo + kTkChunk);
-  constexpr int kPer = kTkChunk / kTkBlock;
-  float x[kPer];
-  bool up[kPer], eq[kPer];
-  uint32_t lup[kPer], lcand[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int idx = lo + i * kTkBlock + tid;
-    const bool valid = idx < hi;
-    x[i] = valid ? row[idx] : 0.0f;
-    const uint32_t b = bin_of(x[i]);
-    up[i] = valid && b > T;
-    eq[i] = valid && b == T;
-    lup[i] = wave_reserve(&s.emit, up[i]);
-    lcand[i] = wave_reserve(&s.ncand, eq[i]);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    s.base_up = s.emit ? atomicAdd(&ctr[0], s.emit) : 0u;
-    s.base_cand = s.ncand ? atomicAdd(&ctr[1], s.ncand) : 0u;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int idx = lo + i * kTkBlock + tid;
-    const uint32_t pos = s.base_up + lup[i];
-    if (up[i] && pos < (uint32_t)m) out[pos] = idx;
-    const uint32_t cpos = s.base_cand + lcand[i];
-    if (eq[i] && cpos < (uint32_t)kTkCand) gcand[cpos] = composite_key(x[i], idx);
-  }
-}
-
-// Long rows, third launch: one workgroup per row resolves the boundary bin
-// from the candidate list (or by re-reading the row if the list overflowed)
-// and leaves the row's workspace zero-filled.  The kernel boundaries between
-// the three launches make every workgroup's writes visible without fences.
-__global__ __launch_bounds__(kTkBlock) void topk_long_finish_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
-    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws) {
-  __shared__ TopkShared s;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const int n = max(0, min(row_len[r], max_len));
-  if (n < kTkLongMin) return;
-  const int m = k;
-  const float* row = scores + (int64_t)r * ld;
-  int32_t* out = sel + (int64_t)r * k;
-  uint8_t* rec = ws_row(ws, r);
+  uint8_t* rec = ws + (size_t)r * kWsRow;
   uint32_t* gh = reinterpret_cast<uint32_t*>(rec + kWsHist);
   uint32_t* ctr = reinterpret_cast<uint32_t*>(rec + kWsCtr);
   uint64_t* gcand = reinterpret_cast<uint64_t*>(rec + kWsCand);
-  const uint32_t nc = ctr[1], T = ctr[2], above = ctr[3];
-  const uint32_t need = (uint32_t)m - above;
-  if (tid == 0) s.emit = above;
-  if (nc <= (uint32_t)kTkCand)
-    for (int i = tid; i < (int)nc; i += kTkBlock) s.cand[i] = gcand[i];
+
+  const RowReader rd(row, n);
+  float x[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) x[i] = rd[lo + i * kLongNT + tid];
+  for (int i = tid; i < kBins; i += kLongNT) s.hist[i] = gh[i];
+  RowGeom g{};
+  int first_lp = 0;
+  if (TRANSLATE) {
+    // The chunk's blocks [lo, lo + kChunk) cover at most 256 logical pages.
+    g = row_geometry(tr, r);
+    first_lp = (tr.c * lo) >> 6;
+    const int lp = first_lp + tid;
+    s.pages[tid] = lp < tr.pt_stride ? tr.page_table[(int64_t)g.b * tr.pt_stride + lp] : -1;
+  }
   __syncthreads();
-  if (nc <= (uint32_t)kTkCand) refine<false>(s, row, n, T, nc, need, out, m);
-  else refine<true>(s, row, n, T, nc, need, out, m);
+  threshold_to_shared(s, (uint32_t)m);
+  const uint32_t T = s.T, above = s.above;
+
+  // Count, block scan, one device atomic per list for the workgroup.
+  uint32_t nup = 0, neq = 0;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const bool valid = lo + i * kLongNT + tid < n;
+    const uint32_t b = bin_of(x[i]);
+    nup += (valid && b > T) ? 1u : 0u;
+    neq += (valid && b == T) ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t excl = block_excl_scan<kLongNT>(s, (nup << 20) | neq, total);
+  if (tid == 0) {
+    s.base_up = (total >> 20) ? __hip_atomic_fetch_add(&ctr[1], total >> 20, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    s.base_cand = (total & 0xFFFFFu) ? __hip_atomic_fetch_add(&ctr[2], total & 0xFFFFFu, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT) : 0u;
+  }
+  // Stage this workgroup's picks in LDS at their scanned offsets (the
+  // running per-lane counters keep each lane's picks in index order), then
+  // write them out with all lanes: coalesced stores, no divergent loop.
+  uint32_t lu = excl >> 20, le = excl & 0xFFFFFu;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int idx = lo + i * kLongNT + tid;
+    if (idx < n) {
+      const uint32_t b = bin_of(x[i]);
+      if (b > T) {
+        if (lu < (uint32_t)kKmax) s.chosen[lu] = idx;
+        ++lu;
+      } else if (b == T) {
+        if (le < (uint32_t)kLongCand) s.cand[le] = composite_key(x[i], idx);
+        ++le;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t tot_up = min(total >> 20, (uint32_t)kKmax), tot_eq = min(total & 0xFFFFFu, (uint32_t)kLongCand);
+  for (uint32_t j = tid; j < tot_up; j += kLongNT) {
+    const uint32_t pos = s.base_up + j;
+    if (pos < (uint32_t)m) {
+      const int idx = s.chosen[j];
+      out[pos] = idx;
+      if (TRANSLATE) {
+        if (tr.c == 1) translate_block_lds<1>(tr, r, (int)pos, idx, s.pages, first_lp);
+        else translate_block_lds<4>(tr, r, (int)pos, idx, s.pages, first_lp);
+      }
+    }
+  }
+  for (uint32_t j = tid; j < tot_eq; j += kLongNT) {
+    const uint32_t cpos = s.base_cand + j;
+    if (cpos < (uint32_t)kLongCand)
+      __hip_atomic_store(&gcand[cpos], s.cand[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Every lane's candidate stores have completed before the chunk arrives.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s.last = __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(nchunk - 1);
+  __syncthreads();
+  if (!s.last) return;
+
+  // The last chunk to arrive resolves the boundary bin.
+  const uint32_t nc = __hip_atomic_load(&ctr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t need = (uint32_t)m - above;
+  if (nc <= (uint32_t)kLongCand)
+    for (int i = tid; i < (int)nc; i += kLongNT)
+      s.cand[i] = __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (need >= 1 && need <= (uint32_t)m) {
+    if (nc <= (uint32_t)kLongCand) {
+      if (need >= nc) {
+        for (uint32_t i = tid; i < nc; i += kLongNT) {
+          const uint32_t at = above + i;
+          if (at < (uint32_t)m) {
+            const int idx = index_of(s.cand[i]);
+            out[at] = idx;
+            s.chosen[at] = idx;
+          }
+        }
+      } else {
+        block_refine<kLongNT, kLongCand>(s, nc, need, out, s.chosen, above, m);
+      }
+      __syncthreads();
+    } else {
+      if (tid == 0) s.emit = above;
+      __syncthreads();
+      block_refine_from_row<kLongNT, kLongCand>(s, row, n, T, need, out, s.chosen, m);
+    }
+  }
   if (tid == 0) sel_count[r] = m;
+  if (TRANSLATE) {
+    for (int q = (int)above + tid; q < m; q += kLongNT) translate_block(tr, g, r, q, s.chosen[q]);
+    translate_tail<kLongNT>(tr, g, r, m);
+  }
   // Leave the row's workspace zero-filled for the next call.
-  gh[tid] = 0;
-  if (tid < 16) ctr[tid] = 0;
-  const int used = (int)min(nc, (uint32_t)kTkCand);
-  for (int i = tid; i < used; i += kTkBlock) gcand[i] = 0;
+  for (int i = tid; i < kBins; i += kLongNT) __hip_atomic_store(&gh[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < 16) __hip_atomic_store(&ctr[tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int used = (int)min(nc, (uint32_t)kLongCand);
+  for (int i = tid; i < used; i += kLongNT)
+    __hip_atomic_store(&gcand[i], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+static bool use_long_path(int32_t num_rows, int32_t max_len) {
+  return max_len >= kLongMin && num_rows <= kLongRowsMax;
 }
 
 size_t topk_workspace_size(int32_t num_rows, int32_t max_len, int32_t /*k*/) {
-  return max_len >= kTkLongMin ? (size_t)num_rows * kWsRow : 0;
+  return use_long_path(num_rows, max_len) ? (size_t)num_rows * kWsRow : 0;
+}
+
+template <bool TRANSLATE>
+static int launch_select(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows, int32_t max_len,
+                         int32_t k, int32_t* sel, int32_t* sel_count, void* workspace, const Translate& tr,
+                         hipStream_t stream) {
+  if (use_long_path(num_rows, max_len)) {
+    const int nchunk = (max_len + kChunk - 1) / kChunk;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    hipLaunchKernelGGL(topk_long_hist_kernel<TRANSLATE>, dim3(num_rows, nchunk), dim3(kLongNT), 0, stream, scores,
+                       ld, row_len, max_len, k, sel, sel_count, ws, tr);
+    if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
+    hipLaunchKernelGGL(topk_long_emit_kernel<TRANSLATE>, dim3(num_rows, nchunk), dim3(kLongNT), 0, stream, scores,
+                       ld, row_len, max_len, k, sel, sel_count, ws, tr);
+  } else {
+    hipLaunchKernelGGL(topk_rows_kernel<TRANSLATE>, dim3(num_rows), dim3(kRowNT), 0, stream, scores, ld, row_len,
+                       max_len, k, sel, sel_count, tr);
+  }
+  return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
 }
 
 int launch_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows, int32_t max_len,
                 int32_t k, int32_t* sel, int32_t* sel_count, void* workspace, hipStream_t stream) {
-  const bool any_long = max_len >= kTkLongMin;
-  const int nchunk = any_long ? (max_len + kTkChunk - 1) / kTkChunk : 1;
-  dim3 grid(num_rows, nchunk), block(kTkBlock);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hipLaunchKernelGGL(topk_main_kernel, grid, block, 0, stream, scores, ld, row_len, max_len, k, sel,
-                     sel_count, ws);
-  if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
-  if (any_long) {
-    hipLaunchKernelGGL(topk_long_emit_kernel, grid, block, 0, stream, scores, ld, row_len, max_len, k, sel, ws);
-    if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
-    hipLaunchKernelGGL(topk_long_finish_kernel, dim3(num_rows), block, 0, stream, scores, ld, row_len, max_len,
-                       k, sel, sel_count, ws);
-    if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
-  }
-  return BS_OK;
+  const Translate none{};
+  return launch_select<false>(scores, ld, row_len, num_rows, max_len, k, sel, sel_count, workspace, none, stream);
+}
+
+int launch_select_translate(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows,
+                            int32_t max_len, int32_t k, const int32_t* req_row_ptr, int32_t num_req,
+                            const int32_t* row_pos, int32_t c, const int32_t* page_table, int32_t pt_stride,
+                            int32_t* sel, int32_t* sel_count, int32_t* out_slots, int32_t* out_pos,
+                            int32_t* out_count, int32_t ld_out, void* workspace, hipStream_t stream) {
+  const Translate tr{req_row_ptr, num_req, row_pos, c, page_table, pt_stride, out_slots, out_pos, out_count, ld_out};
+  return launch_select<true>(scores, ld, row_len, num_rows, max_len, k, sel, sel_count, workspace, tr, stream);
 }
 
 }  // namespace bs

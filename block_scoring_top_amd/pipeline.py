@@ -8,8 +8,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (idx_expand_translate, idx_score_decode, idx_score_prefill, topk_select_rows,
-               topk_workspace)
+from . import (idx_expand_translate, idx_score_decode, idx_score_prefill, idx_select_translate,
+               topk_select_rows, topk_workspace)
 
 
 class IndexerPath:
@@ -54,7 +54,19 @@ class IndexerPath:
         idx_expand_translate(self.sel, self.sel_count, i.k, i.req_row_ptr, i.row_pos, i.c, i.page_table,
                              self.slots, self.out_count, out_pos=self.pos, stream=stream)
 
-    def run(self, stream=None):
+    def select_translate(self, stream=None):
+        """Top-k and expand/translate fused in one kernel."""
+        i = self.inp
+        idx_select_translate(self.scores, self.row_len, int(i.max_vis), i.k, i.req_row_ptr, i.row_pos, i.c,
+                             i.page_table, self.sel, self.sel_count, self.slots, self.out_count, out_pos=self.pos,
+                             workspace=self.workspace, stream=stream)
+
+    def run(self, stream=None, fused: bool = True):
+        """One pass of the path: score, then select + translate (fused into one
+        kernel, the default) or the separate select and expand calls."""
         self.score(stream)
-        self.select(stream)
-        self.expand(stream)
+        if fused:
+            self.select_translate(stream)
+        else:
+            self.select(stream)
+            self.expand(stream)

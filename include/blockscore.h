@@ -156,9 +156,10 @@ size_t topk_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k);
  * to an order-preserving 16-bit key whose upper 10 bits index a 1,024-bin
  * histogram; the bin holding the m-th largest is located, entries in higher
  * bins are emitted directly, and the boundary bin is resolved exactly on the
- * (FP32 key, index) pair by radix selection.  Short rows are kept in
- * registers, medium rows stream through one workgroup, long rows are split
- * over several workgroups whose histograms merge through device-scope atomics.
+ * (FP32 key, index) pair by radix selection.  In a large batch each row is
+ * done by one workgroup (in registers up to 16,384 entries, else streamed);
+ * in a small batch (<= 256 rows) rows of >= 32,769 entries are split over
+ * several workgroups whose histograms merge through device-scope atomics.
  * Device preconditions: row_len[r] >= 0 (negative counts as 0); no NaN
  * (a NaN is ordered above +inf or below -inf by its sign bit).
  * Returns BS_OK, BS_ERR_NULL, BS_ERR_ARG (k outside 1..2048, max_len < 0,
@@ -192,6 +193,25 @@ int idx_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_t k
                          const int32_t* page_table, int32_t pt_stride,
                          int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
                          int32_t ld_out, void* stream);
+
+/*
+ * idx_select_translate - topk_select_rows and idx_expand_translate in one
+ * kernel [TOPK: the selection and the page-table transform fused to cut
+ * latency; QSA: expansion and pending append].
+ *
+ * Same selection as topk_select_rows (same arguments, workspace and
+ * guarantees for scores .. sel_count) and, for each row, the same expansion,
+ * append and translation of that selection as idx_expand_translate (same
+ * arguments and guarantees for req_row_ptr .. ld_out); the slots follow the
+ * order of the row's entries in sel.  Errors: the union of both calls'.
+ */
+int idx_select_translate(const float* scores, int64_t ld_scores, const int32_t* row_len,
+                         int32_t num_rows, int32_t max_len, int32_t k,
+                         const int32_t* req_row_ptr, int32_t num_req, const int32_t* row_pos, int32_t c,
+                         const int32_t* page_table, int32_t pt_stride,
+                         int32_t* sel, int32_t* sel_count,
+                         int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* bs_status_string - a static, human-readable name for a status code. */
 const char* bs_status_string(int status);

@@ -17,11 +17,12 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def run_path(inp, scorer: str = "decode"):
-    say(f"path {scorer}: {getattr(inp, 'name', '?')} rows={inp.num_rows} max_vis={inp.max_vis} k={inp.k} c={inp.c}")
+def run_path(inp, scorer: str = "decode", fused: bool = True):
+    say(f"path {scorer} fused={fused}: {getattr(inp, 'name', '?')} rows={inp.num_rows} max_vis={inp.max_vis} "
+        f"k={inp.k} c={inp.c}")
     dev = upload(inp, "cuda")
     p = IndexerPath(dev, scorer)
-    p.run()
+    p.run(fused=fused)
     torch.cuda.synchronize()
     return dict(scores=p.scores.cpu().numpy(), row_len=p.row_len.cpu().numpy(), sel=p.sel.cpu().numpy(),
                 sel_count=p.sel_count.cpu().numpy(), slots=p.slots.cpu().numpy(), pos=p.pos.cpu().numpy(),

@@ -19,11 +19,11 @@ pytestmark = pytest.mark.gpu
 gu = pytest.importorskip("gpu_util")
 
 
-def _full_check(inp, scorer="decode"):
+def _full_check(inp, scorer="decode", fused=True):
     """Every stage against the oracle: scores (tolerance), top-k of the GPU
     scores (exact), end-to-end selection (band), expand of the GPU selection
-    (exact)."""
-    g = gu.run_path(inp, scorer)
+    (exact).  fused: select + translate in one kernel, else separate calls."""
+    g = gu.run_path(inp, scorer, fused)
     ref = oracle.pipeline(inp)
     assert np.array_equal(g["row_len"], ref["row_len"])
     check_scores(g["scores"], ref["scores"], ref["row_len"])
@@ -40,16 +40,25 @@ def _full_check(inp, scorer="decode"):
 # Decode scorer
 # ---------------------------------------------------------------------------
 
-def test_decode_cfg_qsa_1x8k_end_to_end():
-    _full_check(synth.qsa_decode_1x8k())
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_cfg_qsa_1x8k_end_to_end(fused):
+    _full_check(synth.qsa_decode_1x8k(), fused=fused)
 
 
-def test_decode_verify_small_ragged():
-    _full_check(synth.qsa_verify_64req(B=8, lo=300, hi=20000))
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_verify_small_ragged(fused):
+    _full_check(synth.qsa_verify_64req(B=8, lo=300, hi=20000), fused=fused)
 
 
-def test_decode_dsa_small():
-    _full_check(synth.dsa_decode_16x80k(B=3, L=5000))
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_dsa_small(fused):
+    _full_check(synth.dsa_decode_16x80k(B=3, L=5000), fused=fused)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_dsa_long_rows_small_batch(fused):
+    # few long rows: the multi-workgroup selection (and its fused translation)
+    _full_check(synth.dsa_decode_16x80k(B=3, L=50000), fused=fused)
 
 
 def test_decode_edge_rows():
@@ -198,8 +207,47 @@ def test_e2e_verify_64req_full():
     _full_check(synth.qsa_verify_64req())
 
 
-def test_e2e_dsa_16x80k_full():
-    _full_check(synth.dsa_decode_16x80k())
+@pytest.mark.parametrize("fused", [True, False])
+def test_e2e_dsa_16x80k_full(fused):
+    _full_check(synth.dsa_decode_16x80k(), fused=fused)
+
+
+def test_fused_select_translate_on_given_rows():
+    # idx_select_translate on given FP32 rows (tie storms, long and short rows
+    # in one batch) against the oracle's top-k and expand of the same rows
+    import torch
+    import block_scoring_top_amd as bst
+    from synth.device import upload
+    rng = np.random.default_rng(41)
+    ctx = [90000, 70000, 3000, 40000]
+    inp = synth.build_paged_batch("fs", 41, c=1, k=2048, ctx_tokens=ctx, row_pos_per_req=[[t - 1] for t in ctx],
+                                  rng=rng)
+    lens = ((inp.row_pos + 1) // inp.c).astype(np.int32)
+    ld = int(lens.max())
+    rows = synth.tie_storm_rows(42, 4, ld)
+    rows[0] = rng.standard_normal(ld).astype(np.float32)
+    dev = upload(inp, "cuda")
+    s = torch.from_numpy(rows).cuda()
+    rl = torch.from_numpy(lens).cuda()
+    R = inp.num_rows
+    sel = torch.empty((R, inp.k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(R, dtype=torch.int32, device="cuda")
+    slots = torch.empty((R, inp.ld_out), dtype=torch.int32, device="cuda")
+    pos = torch.empty((R, inp.ld_out), dtype=torch.int32, device="cuda")
+    oc = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws = bst.topk_workspace(R, ld, inp.k, "cuda")
+    for rep in range(3):
+        gu.say(f"select_translate rep {rep}")
+        bst.idx_select_translate(s, rl, ld, inp.k, dev.req_row_ptr, dev.row_pos, inp.c, dev.page_table, sel, cnt,
+                                 slots, oc, out_pos=pos, workspace=ws)
+        torch.cuda.synchronize()
+        ref_sel, ref_cnt = oracle.topk(rows, lens, inp.k)
+        check_topk_exact(sel.cpu().numpy(), cnt.cpu().numpy(), ref_sel, ref_cnt)
+        rs, rp, rc = oracle.expand_translate(inp, sel.cpu().numpy(), cnt.cpu().numpy())
+        check_expand_exact(slots.cpu().numpy(), pos.cpu().numpy(), oc.cpu().numpy(), rs, rp, rc,
+                           gu.pending_counts(inp))
+    if ws is not None:
+        assert int(ws.count_nonzero().item()) == 0
 
 
 # ---------------------------------------------------------------------------
