@@ -24,9 +24,15 @@ CFLAGS = [
 ]
 
 
+# Per-source extras.  The prefill scorer keeps its MFMA accumulators in
+# architectural VGPRs (gfx950 allows either file): its epilogue then reads them
+# without v_accvgpr moves, at the same occupancy.
+EXTRA = {"score_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, objdir: str, verbose: bool) -> str:
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)

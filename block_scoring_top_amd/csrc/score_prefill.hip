@@ -16,8 +16,10 @@
 //     key tiles; each wave keeps its 16 rows' q fragments in registers for the
 //     whole loop;
 //   * 64-key tiles are gathered through the page table into LDS (rows padded
-//     to 272 bytes so 16-byte fragment reads are bank-conflict free), double
-//     buffered so the next tile's global loads overlap this tile's MFMAs;
+//     to 272 bytes so 16-byte fragment reads are bank-conflict free), triple
+//     buffered so tile t+2's global loads overlap tile t's MFMAs; the page
+//     ids of the workgroup's key range are staged in LDS once, so no key load
+//     waits on a page-table load;
 //   * causal visibility: tiles past the block's last visible key are skipped,
 //     and per-row masking happens at the store.
 #include "device.h"
@@ -29,10 +31,15 @@ constexpr int kPfRows = 64;         // query rows per workgroup, 16 per wave
 constexpr int kPfKeys = 64;         // keys per tile
 constexpr int kPfStride = 272;      // LDS bytes per key row (256 + 16 pad)
 constexpr int kPfTileBytes = kPfKeys * kPfStride;
+constexpr int kPfMaxTiles = 64;     // key tiles per workgroup (host sizing)
+constexpr int kPfMaxPages = kPfMaxTiles * kPfKeys * 4 / kPage;  // logical pages they span (c = 4)
 
+// Loads this lane's four 16-byte slices of a 64-key tile (keys j0 ..
+// j0+63; slice e covers key (e*256 + lane) / 16, dims 8*((e*256 + lane) % 16)).
+// Page ids come from the workgroup's LDS copy (lp0 = its first logical page).
 __device__ __forceinline__ void pf_load_tile(const uint16_t* __restrict__ kcache, int64_t num_pages,
-                                             const int32_t* __restrict__ pt, int per_page, int c,
-                                             int j0, int nmax, u32x4_t (&regs)[4]) {
+                                             const int32_t* pages, int lp0, int per_page, int c, int j0, int nmax,
+                                             u32x4_t (&regs)[4]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -41,10 +48,10 @@ __device__ __forceinline__ void pf_load_tile(const uint16_t* __restrict__ kcache
     const int j = j0 + n;
     regs[e] = u32x4_t{0u, 0u, 0u, 0u};
     if (j < nmax) {
-      const int32_t page = pt[(c * j) >> 6];
+      const int32_t page = pages[((c * j) >> 6) - lp0];
       if (page >= 0 && page < num_pages) {
         const int64_t slot = (int64_t)page * per_page + (j & (per_page - 1));
-        regs[e] = *(reinterpret_cast<const u32x4_t*>(kcache + slot * kDim) + slice);
+        regs[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kcache + slot * kDim) + slice);
       }
     }
   }
@@ -65,7 +72,8 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     const int32_t* __restrict__ page_table, int32_t pt_stride,
     const int32_t* __restrict__ req_row_ptr, int32_t num_req, const int32_t* __restrict__ row_pos,
     int32_t c, int32_t max_vis, float* __restrict__ scores, int64_t ld, int32_t* __restrict__ row_len) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPfTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3][kPfTileBytes];
+  __shared__ int32_t pages[kPfMaxPages];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // Work item -> (request, block of 64 rows).
@@ -115,21 +123,34 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
     const int orow = rb0 + wave * 16 + ms * 4 + g;
     nvis[ms] = orow < rb1 ? min((row_pos[orow] + 1) / c, max_vis) : 0;
   }
+  // Smallest visible length over the wave's 16 rows (rows past the block
+  // count as 0, so a partial block always takes the masked path).
+  int wave_min_vis = min(min(nvis[0], nvis[1]), min(nvis[2], nvis[3]));
+  for (int off = 16; off < 64; off <<= 1) wave_min_vis = min(wave_min_vis, __shfl_xor(wave_min_vis, off));
 
+  // The page ids of this workgroup's key range, once: key loads then depend
+  // on LDS, not on a global page-table load.
+  const int lp0 = (c * t0 * kPfKeys) >> 6;
+  const int lp1 = min(pt_stride, ((c * (t1 * kPfKeys) - 1) >> 6) + 1);
+  for (int i = tid; i < lp1 - lp0 && i < kPfMaxPages; i += 256) pages[i] = pt[lp0 + i];
+  __syncthreads();
+
+  // Three LDS buffers: tile t is computed while tile t+1 sits in LDS and the
+  // loads of tile t+2 are in flight.
   u32x4_t pre[4];
-  pf_load_tile(kcache, num_pages, pt, per_page, c, t0 * kPfKeys, nmax, pre);
+  pf_load_tile(kcache, num_pages, pages, lp0, per_page, c, t0 * kPfKeys, nmax, pre);
   pf_store_tile(lds[0], pre);
+  if (t0 + 1 < t1) pf_load_tile(kcache, num_pages, pages, lp0, per_page, c, (t0 + 1) * kPfKeys, nmax, pre);
   __syncthreads();
 
   for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
-    if (t + 1 < t1) pf_load_tile(kcache, num_pages, pt, per_page, c, (t + 1) * kPfKeys, nmax, pre);
+    const int buf = (t - t0) % 3;
+    u32x4_t nxt[4];
+    if (t + 2 < t1) pf_load_tile(kcache, num_pages, pages, lp0, per_page, c, (t + 2) * kPfKeys, nmax, nxt);
+    if (t + 1 < t1) pf_store_tile(lds[(t + 1 - t0) % 3], pre);
     const uint8_t* tile = lds[buf];
     f32x4_t acc[4][4];
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
 #pragma unroll
@@ -137,24 +158,27 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(
         const bf16x8_t bfr = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const u32x4_t*>(tile + (ns * 16 + i16) * kPfStride + (32 * ks + 8 * g) * 2));
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-          acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], bfr, acc[ms][ns], 0, 0, 0);
+        for (int ms = 0; ms < 4; ++ms)  // the first k-step starts from C = 0: no accumulator clearing
+          acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], bfr, ks == 0 ? zero : acc[ms][ns], 0, 0, 0);
       }
     }
-    // Epilogue: lane holds heads 0..3 of query row (4*ms + g) for key (16*ns + i16).
+    // Epilogue: lane holds heads 0..3 of query row (4*ms + g) for key
+    // (16*ns + i16).  Tiles wholly inside every row's visible range store
+    // without masks (uniform branch); the causal boundary tile masks per row.
+    const bool full = (t + 1) * kPfKeys <= wave_min_vis;
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
-      const int orow = rb0 + wave * 16 + ms * 4 + g;
-      float* dst = scores + (int64_t)orow * ld;
+      float* dst = scores + (int64_t)(rb0 + wave * 16 + ms * 4 + g) * ld + t * kPfKeys + i16;
+      const int lim = nvis[ms] - t * kPfKeys - i16;  // store column ns*16 iff ns*16 < lim
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) {
-        const int j = t * kPfKeys + ns * 16 + i16;
         const f32x4_t a = acc[ms][ns];
-        const float s = (fmaxf(a.x, 0.f) + fmaxf(a.y, 0.f)) + (fmaxf(a.z, 0.f) + fmaxf(a.w, 0.f));
-        if (j < nvis[ms]) dst[j] = s * kScale;
+        const float sc = ((fmaxf(a.x, 0.f) + fmaxf(a.y, 0.f)) + (fmaxf(a.z, 0.f) + fmaxf(a.w, 0.f))) * kScale;
+        if (full || ns * 16 < lim) dst[ns * 16] = sc;
       }
     }
-    if (t + 1 < t1) pf_store_tile(lds[buf ^ 1], pre);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pre[e] = nxt[e];
     __syncthreads();
   }
 }
@@ -169,9 +193,11 @@ int launch_score_prefill(const uint16_t* q, const uint16_t* kcache, int64_t num_
   const int64_t blocks = (int64_t)(num_rows + kPfRows - 1) / kPfRows + num_req;
   const int64_t tiles = ((int64_t)max_vis + kPfKeys - 1) / kPfKeys;
   int64_t splits = (2048 + blocks - 1) / blocks;
+  const int64_t min_splits = (tiles + kPfMaxTiles - 1) / kPfMaxTiles;  // at most kPfMaxTiles tiles each
+  splits = splits < min_splits ? min_splits : splits;
   splits = splits < 1 ? 1 : splits;
   splits = splits > tiles ? (tiles > 0 ? tiles : 1) : splits;
-  splits = splits > 65535 ? 65535 : splits;
+  if (splits > 65535) return BS_ERR_ARG;
   if (blocks > 0x7FFFFFFF) return BS_ERR_ARG;
   hipLaunchKernelGGL(score_prefill_kernel, dim3((unsigned)blocks, (unsigned)splits), dim3(256), 0, stream, q,
                      kcache, num_pages, page_table, pt_stride, req_row_ptr, num_req, row_pos, c, max_vis, scores,
