@@ -291,3 +291,21 @@ def test_prefill_agrees_with_decode_scorer():
     b, lb = gu.gpu_scores(inp, "decode")
     assert np.array_equal(la, lb)
     check_scores(a, b.astype(np.float64), la, what="prefill vs decode")
+
+
+@pytest.mark.parametrize("extra_ld", [0, 3])
+def test_prefill_c1_ragged_and_row_stride(extra_ld):
+    # c = 1 (one key per token, 64 per page), requests of several 64-row
+    # blocks with ragged tails; extra_ld = 3 gives a row stride that is not a
+    # multiple of 4 floats (the kernel's per-float store path).  Entries past
+    # each row's visible range stay untouched.
+    rng = np.random.default_rng(77)
+    rows = [list(range(1500, 1630)), [0, 1, 2, 63, 64], list(range(3000, 3071)), []]
+    inp = synth.build_paged_batch("pf1", 77, c=1, k=256, ctx_tokens=[1630, 65, 3071, 9], row_pos_per_req=rows,
+                                  rng=rng)
+    s, rl = gu.gpu_scores(inp, "prefill", ld=inp.max_vis + extra_ld)
+    ref = oracle.pipeline(inp)
+    assert np.array_equal(rl, ref["row_len"])
+    check_scores(s[:, :inp.max_vis], ref["scores"], ref["row_len"])
+    for r in range(inp.num_rows):
+        assert np.all(np.isnan(s[r, rl[r]:]))
