@@ -16,16 +16,20 @@
 //     consecutive keys of one row and stores them with one 16-byte store;
 //   * a workgroup (4 waves) owns 64 query rows of one request at a time; each
 //     wave keeps its 16 rows' q fragments in registers;
-//   * 64-key tiles pass through LDS, double buffered: the next tile's global
-//     loads are in flight while the current tile is multiplied.  Each wave
-//     loads 16 consecutive keys of a tile, which lie in one page (a page holds
-//     64/c >= 16 keys for c <= 4), so the page lookup and the bounds are
-//     wave-uniform: one scalar page-table read and one buffer resource per
-//     wave per tile, whose range check zero-fills keys past the visible range
-//     or behind an invalid page id;
+//   * 64-key tiles are copied from HBM straight into LDS (buffer loads with
+//     the LDS flag: no staging registers, no LDS write instructions), three
+//     buffers, two tiles ahead.  Each wave copies 16 consecutive keys of a
+//     tile, which lie in one page (a page holds 64/c >= 16 keys for c <= 4),
+//     so the page lookup and the bounds are wave-uniform: one scalar
+//     page-table read and one buffer resource per wave per tile, whose range
+//     check zero-fills keys past the visible range or behind an invalid page
+//     id.  A tile's 16 B fragments are read from LDS before its 64 MFMAs, so
+//     the reads are in flight together;
 //   * the LDS tile is unpadded with an XOR swizzle (the 16-byte slice s of
-//     key n sits at slot s ^ ((n / 4) mod 16)), so the fragment reads and the
-//     tile writes are free of bank conflicts;
+//     key n sits at slot s ^ ((n / 4) mod 16)), so the fragment reads are free
+//     of bank conflicts;
+//   * scores are written with non-temporal stores (they are read once, by the
+//     selection, after the whole launch);
 //   * work is the list of (64-row block, key tile) units, split into equal
 //     contiguous ranges over a grid sized to the chip's resident workgroups;
 //     tiles past a block's causal limit are skipped.
@@ -40,6 +44,7 @@ constexpr int kPfRows = 64;                       // query rows per block, 16 pe
 constexpr int kPfKeys = 64;                       // keys per tile
 constexpr int kPfTileBytes = kPfKeys * kDim * 2;  // 16 KiB
 constexpr int kPfGroup = 16;                      // keys loaded per wave per tile
+constexpr int kPfBufs = 3;                        // LDS tile buffers
 
 // Locates 64-row block `bi` (blocks are numbered request by request):
 // returns false if there is no such block.
@@ -67,6 +72,30 @@ __device__ __forceinline__ float head_sum(const f32x4_t& a) {
   return ((relu_bits(a.x) + relu_bits(a.y)) + (relu_bits(a.z) + relu_bits(a.w))) * kScale;
 }
 
+// Loads 64 lanes x 16 bytes from a buffer straight into LDS (no VGPRs): lane
+// i reads at byte `voffset` of the resource and writes LDS bytes
+// lds_addr + 16*i .. +15 (M0 holds the wave-uniform LDS address).  The
+// transfer is counted by vmcnt; the caller waits with s_waitcnt before a
+// barrier publishes the data.  Out-of-range lanes of the resource write zeros.
+__device__ __forceinline__ void lds_dma_b128(const u32x4_t& rsrc, uint32_t voffset, uint32_t lds_addr) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)rsrc.y << 32) | rsrc.x), (short)0, rsrc.z, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds_addr, 16, voffset, 0, 0, 0);
+}
+
+// vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without a memory fence: __syncthreads() would also wait
+// for this wave's outstanding global stores.  The asm is a compiler barrier
+// for memory operations; LDS data written by the transfers above is published
+// by the caller's vmcnt wait before it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <bool VEC>
 __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kcache, int64_t num_pages,
@@ -74,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
     const int32_t* __restrict__ req_row_ptr, int32_t num_req, const int32_t* __restrict__ row_pos,
     int32_t num_rows, int32_t c, int32_t max_vis, int32_t tiles_per_block, int64_t units,
     float* __restrict__ scores, int64_t ld, int32_t* __restrict__ row_len) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPfTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kPfBufs][kPfTileBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
@@ -90,18 +119,18 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
   // Page ids are int32: a bound above 2^31 - 1 admits every non-negative id.
   const int32_t num_pages32 = num_pages > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)num_pages;
 
-  // Per-lane constant LDS offsets.  Tile write: slice lane % 16 of key
-  // 16*wave + 4*e + lane/16 (whose key group E = 4*wave + e).  Fragment read
-  // for k-step ks: key 4*i16 + ns (ns*256 added as an immediate), slice
-  // 4*ks + g.
-  uint32_t wofs[4], rofs[4];
+  // LDS tile layout: key n at bytes 256*n, its 16-byte slice s at slot
+  // s ^ ((n / 4) mod 16).  Tile load: instruction e of a wave fills keys
+  // 16*wave + 4*e .. +3 (1 KiB, key group E = 4*wave + e), lane i the slot
+  // i % 16 of key 16*wave + 4*e + i/16, i.e. slice (i % 16) ^ E, read at this
+  // byte offset from the wave's first key.  Fragment read for k-step ks: key
+  // 4*i16 + ns (ns*256 added as an immediate), slice 4*ks + g.
+  uint32_t vofs[4], rofs[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int E = 4 * wave + e;
-    wofs[e] = (uint32_t)((16 * wave + 4 * e + (lane >> 4)) * 256 + 16 * ((lane & 15) ^ E));
-  }
+  for (int e = 0; e < 4; ++e) vofs[e] = (uint32_t)(e * 1024 + (lane >> 4) * 256 + 16 * ((lane & 15) ^ (4 * wave + e)));
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) rofs[ks] = (uint32_t)(i16 * 1024 + 16 * ((4 * ks + g) ^ i16));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(&lds[0][0]);
 
   for (int64_t u = u0; u < u1;) {
     const int64_t bi = u / tiles_per_block;
@@ -148,86 +177,100 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
 
     const int32_t* pt = page_table + (int64_t)b * pt_stride;
     // This wave's 16 keys of tile t start at key jw = 64*t + 16*wave: their
-    // page id (-1 past the block's visible range), read one tile ahead.
+    // page id, or -1 at or past the block's visible range.  The table index
+    // is clamped so that the (scalar) read is unconditional.
     auto group_page = [&](int t) -> int32_t {
       const int jw = t * kPfKeys + kPfGroup * wave;
-      return jw < nmax ? pt[(c * jw) >> 6] : -1;
+      const int32_t id = pt[min((c * jw) >> 6, pt_stride - 1)];
+      return jw < nmax ? id : -1;
     };
-    // Buffer resource over those keys: based at the slot of key jw, covering
-    // the keys below nmax, empty if the page id is invalid.
-    auto load_group = [&](int t, int32_t page, u32x4_t(&regs)[4]) {
+    // Issues tile t's loads for this wave into LDS buffer `buf`: always 4
+    // transfers (an invalid page or a tile past the range gives an empty
+    // resource, so zeros), so the vmcnt arithmetic below is fixed.
+    auto dma_group = [&](int t, int32_t page, int buf) {
       const int jw = t * kPfKeys + kPfGroup * wave;
-      const uint16_t* base = kcache;
-      int bytes = 0;
-      if (page >= 0 && page < num_pages32) {
-        base = kcache + ((int64_t)page * per_page + (jw & (per_page - 1))) * kDim;
-        bytes = min(nmax - jw, kPfGroup) * kDim * 2;
+      uint64_t base = reinterpret_cast<uint64_t>(kcache);
+      uint32_t bytes = 0;
+      if (page >= 0 && page < num_pages32 && jw < nmax) {
+        base += (uint64_t)(((int64_t)page * per_page + (jw & (per_page - 1))) * kDim * 2);
+        bytes = (uint32_t)(min(nmax - jw, kPfGroup) * kDim * 2);
       }
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes, 0x00020000);
+      const u32x4_t rs = u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, 0x00020000u};
+      const uint32_t dst = lds0 + (uint32_t)(buf * kPfTileBytes + wave * 4096);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) regs[e] = __builtin_amdgcn_raw_buffer_load_b128(rs, e * 1024 + lane * 16, 0, 0);
-    };
-    auto store_group = [&](uint8_t* buf, const u32x4_t(&regs)[4]) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4_t*>(buf + wofs[e]) = regs[e];
+      for (int e = 0; e < 4; ++e) lds_dma_b128(rs, vofs[e], dst + e * 1024);
     };
 
-    u32x4_t stage[4];
-    load_group(t0, group_page(t0), stage);
-    int32_t page_next = t0 + 1 < t1 ? group_page(t0 + 1) : -1;
-    store_group(lds[0], stage);
-    __syncthreads();
-
-    for (int t = t0; t < t1; ++t) {
-      const int cur = (t - t0) & 1;
-      const bool more = t + 1 < t1;
-      if (more) load_group(t + 1, page_next, stage);  // in flight during this tile
-      const uint8_t* tile = lds[cur];
-      f32x4_t acc[4][4];
+    // Tile products from LDS buffer `buf`: the tile's 16 B fragments are
+    // read first (all in flight at once), then the 64 MFMAs consume them in
+    // order.
+    auto mfma_tile = [&](f32x4_t(&acc)[4][4], int buf) {
+      const uint8_t* tile = lds[buf];
+      bf16x8_t bfr[4][4];
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          bfr[ns][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(tile + rofs[ks] + ns * 256));
       const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
+      for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8_t bfr =
-              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(tile + rofs[ks] + ns * 256));
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int ms = 0; ms < 4; ++ms)  // the first k-step starts from C = 0
             acc[ms][ns] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], bfr, ks == 0 ? zero : acc[ms][ns], 0, 0, 0);
-        }
-      }
-      // The page id for tile t+2 (a scalar load; waited on at the barrier).
-      if (t + 2 < t1) page_next = group_page(t + 2);
-      // Epilogue: lane holds heads 0..3 of query row 4*ms + g for keys
-      // 4*i16 + ns, ns = 0..3.
-      f32x4_t v[4];
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], bfr[ns][ks], ks == 0 ? zero : acc[ms][ns], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // the 16 LDS reads first
+      __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);  // then the MFMAs
+    };
+    // Epilogue values: lane holds heads 0..3 of query row 4*ms + g for keys
+    // 4*i16 + ns, ns = 0..3.
+    auto head_sums = [&](const f32x4_t(&acc)[4][4], f32x4_t(&v)[4]) {
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms)
         v[ms] = f32x4_t{head_sum(acc[ms][0]), head_sum(acc[ms][1]), head_sum(acc[ms][2]), head_sum(acc[ms][3])};
-      // The next tile goes to LDS before this tile's scores are stored, so
-      // that waiting for its loads never waits for these stores.
-      if (more) store_group(lds[cur ^ 1], stage);
-      __builtin_amdgcn_sched_barrier(0);
-      // Tiles inside the visible range of every row of the wave store
-      // without masks.
+    };
+    // Tiles inside the visible range of every row of the wave store without
+    // masks.
+    auto store_tile = [&](const f32x4_t(&v)[4], int t) {
       const bool full = (t + 1) * kPfKeys <= wmin;
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) {
         float* dst = scores + (int64_t)(rb0 + wave * 16 + ms * 4 + g) * ld + t * kPfKeys + 4 * i16;
         if (VEC && full) {
-          *reinterpret_cast<f32x4_t*>(dst) = v[ms];
+          __builtin_nontemporal_store(v[ms], reinterpret_cast<f32x4_t*>(dst));
         } else {
           const int lim = nvis[ms] - t * kPfKeys - 4 * i16;  // keys below lim are visible
-          if (0 < lim) dst[0] = v[ms].x;
-          if (1 < lim) dst[1] = v[ms].y;
-          if (2 < lim) dst[2] = v[ms].z;
-          if (3 < lim) dst[3] = v[ms].w;
+          if (0 < lim) __builtin_nontemporal_store(v[ms].x, dst);
+          if (1 < lim) __builtin_nontemporal_store(v[ms].y, dst + 1);
+          if (2 < lim) __builtin_nontemporal_store(v[ms].z, dst + 2);
+          if (3 < lim) __builtin_nontemporal_store(v[ms].w, dst + 3);
         }
       }
-      __syncthreads();
+    };
+
+    // Pipeline over the block's tiles, three LDS buffers: in step t the
+    // loads of tile t+2 are issued and tile t is multiplied; once tile t+1's
+    // loads are complete the tile's scores are stored.
+    dma_group(t0, group_page(t0), 0);
+    dma_group(t0 + 1, group_page(t0 + 1), 1);
+    int32_t page_ahead = group_page(t0 + 2);
+    wait_vmcnt<4>();  // this wave's part of tile t0 is in LDS
+    barrier_lds();
+    for (int t = t0; t < t1; ++t) {
+      const int i = t - t0;
+      dma_group(t + 2, page_ahead, (i + 2) % kPfBufs);
+      page_ahead = group_page(t + 3);
+      f32x4_t acc[4][4], v[4];
+      mfma_tile(acc, i % kPfBufs);
+      head_sums(acc, v);
+      wait_vmcnt<4>();  // tile t+1 is in LDS (and every older store is done)
+      store_tile(v, t);
+      barrier_lds();
     }
+    wait_vmcnt<0>();  // no transfer into LDS outlives the block
+    __syncthreads();
   }
 }
 
