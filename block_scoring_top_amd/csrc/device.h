@@ -131,6 +131,12 @@ struct RowReader {
   __device__ __forceinline__ float operator[](int idx) const {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, idx * 4, 0, 0));
   }
+  // Entry lane_idx + uniform_idx, the uniform part passed as the scalar
+  // offset, so that loads strided by a constant share one lane offset
+  // register.
+  __device__ __forceinline__ float at(int lane_idx, int uniform_idx) const {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_idx * 4, uniform_idx * 4, 0));
+  }
 };
 
 // Number of set bits of `mask` below this lane.

@@ -45,6 +45,10 @@ namespace bs {
 constexpr int kRowNT = 1024;                   // lanes per workgroup, one row per workgroup
 constexpr int kRowVpt = 16;                    // register path: values per lane
 constexpr int kRowCand = 2048;                 // boundary candidates held in LDS (row kernel)
+constexpr int kManyNT = 256;                   // row kernel for many rows: lanes per workgroup
+constexpr int kManyVpt = 64;                   // ...values per lane in registers
+constexpr int kManyCand = 1024;                // ...boundary candidates in LDS
+constexpr int kManyMinRows = 1024;             // batches with at least this many rows
 constexpr int kLongNT = 256;                   // lanes per workgroup on the long-row kernels
 constexpr int kLongVpt = 16;                   // values per lane held at once there
 constexpr int kLongCand = 4096;
@@ -100,6 +104,24 @@ __device__ __forceinline__ uint32_t inverted_index(int idx) {
   uint32_t r;
   asm volatile("v_not_b32 %0, %1" : "=v"(r) : "v"(idx));
   return r;
+}
+
+// base + i*NT + lane, recomputed at each use: left to itself the compiler
+// keeps all V of these (and their bounds tests) live across the kernel.
+template <int NT>
+__device__ __forceinline__ int entry_index(int base, int i) {
+  int idx = base + i * NT + (int)threadIdx.x;
+  asm volatile("" : "+v"(idx));
+  return idx;
+}
+
+// Makes the compiler treat every value of x as newly produced here (no code
+// is emitted), so that values derived from x earlier are recomputed rather
+// than held in registers across a long stretch.
+template <int V>
+__device__ __forceinline__ void opaque(float (&x)[V]) {
+#pragma unroll
+  for (int i = 0; i < V; ++i) asm volatile("" : "+v"(x[i]));
 }
 
 __device__ __forceinline__ uint64_t composite_key(float v, int idx) {
@@ -362,14 +384,14 @@ __device__ __forceinline__ void block_refine_from_row(TopkShared<CAP>& s, const 
 // positions, then plain writes: no atomics.  up_pos / cand_pos carry the
 // running totals across tiles.
 template <int NT, int V, int CAP>
-__device__ __forceinline__ void emit_tile(TopkShared<CAP>& s, const float (&x)[V], int base, int n, uint32_t T,
+__device__ __forceinline__ void emit_tile(TopkShared<CAP>& s, float (&x)[V], int base, int n, uint32_t T,
                                           uint32_t& up_pos, uint32_t& cand_pos, int m, int32_t* __restrict__ out,
                                           bool keep) {
   const int tid = threadIdx.x;
   uint32_t nup = 0, neq = 0;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    const int idx = base + i * NT + tid;
+    const int idx = entry_index<NT>(base, i);
     const uint32_t b = bin_of(x[i]);
     nup += (idx < n && b > T) ? 1u : 0u;
     neq += (idx < n && b == T) ? 1u : 0u;
@@ -377,10 +399,11 @@ __device__ __forceinline__ void emit_tile(TopkShared<CAP>& s, const float (&x)[V
   uint32_t total;
   const uint32_t excl = block_excl_scan<NT>(s, (nup << 20) | neq, total);
   uint32_t pu = up_pos + (excl >> 20), pe = cand_pos + (excl & 0xFFFFFu);
+  opaque(x);  // the bins are recomputed below, not kept live across the scan
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     __builtin_amdgcn_sched_barrier(0);  // keep one entry's work live at a time
-    const int idx = base + i * NT + tid;
+    const int idx = entry_index<NT>(base, i);
     if (idx < n) {
       const uint32_t b = bin_of(x[i]);
       if (b > T) {
@@ -417,7 +440,7 @@ __device__ __forceinline__ void threshold_to_shared(TopkShared<CAP>& s, uint32_t
 // the histogram (skipped when it is ready), once in NT*V-entry tiles for
 // emission.  HIST_READY: s.hist
 // already holds the row's histogram (long-row finisher).  All lanes call.
-template <int NT, int V, int CAP, bool HIST_READY>
+template <int NT, int V, int CAP, bool HIST_READY, bool STREAM = true>
 __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m,
                                            int32_t* __restrict__ out, bool keep) {
   constexpr int kTile = V;
@@ -428,19 +451,22 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
   uint32_t up_pos = 0, cand_pos = 0;
   uint32_t T, above;
   const RowReader rd(row, n);
-  if (n <= NT * V) {
+  if (!STREAM || n <= NT * V) {  // !STREAM: the caller guarantees n <= NT*V
     float x[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) x[i] = rd[i * NT + tid];
+    for (int i = 0; i < V; ++i) x[i] = rd.at(tid, i * NT);
     if (!HIST_READY) {
 #pragma unroll
-      for (int i = 0; i < V; ++i)
-        if (i * NT + tid < n) atomicAdd(&s.hist[bin_of(x[i])], 1u);
+      for (int i = 0; i < V; ++i) {
+        if (i % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // a few bins live at a time
+        if (entry_index<NT>(0, i) < n) atomicAdd(&s.hist[bin_of(x[i])], 1u);
+      }
     }
     __syncthreads();
     threshold_to_shared(s, (uint32_t)m);
     T = s.T;
     above = s.above;
+    opaque(x);  // as in emit_tile: no histogram bins kept live
     emit_tile<NT, V>(s, x, 0, n, T, up_pos, cand_pos, m, out, keep);
   } else {
     if (!HIST_READY) {
@@ -556,7 +582,7 @@ __device__ __forceinline__ void translate_row(const Translate& tr, int r, int m,
 }
 
 // The whole selection of one row by one workgroup, any n.
-template <int NT, int VPT, int CAP, bool TRANSLATE>
+template <int NT, int VPT, int CAP, bool TRANSLATE, bool STREAM = true>
 __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m, int k,
                                  int32_t* __restrict__ out, int32_t* __restrict__ sel_count, int r,
                                  const Translate& tr) {
@@ -569,7 +595,7 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float
       if (TRANSLATE) s.chosen[i] = i;
     }
   } else {
-    select_row<NT, VPT, CAP, false>(s, row, n, m, out, TRANSLATE);
+    select_row<NT, VPT, CAP, false, STREAM>(s, row, n, m, out, TRANSLATE);
   }
   if (TRANSLATE) {
     __syncthreads();
@@ -577,17 +603,21 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float
   }
 }
 
-// Many rows: one 256-lane workgroup per row.
-template <bool TRANSLATE>
-__global__ __launch_bounds__(kRowNT) void topk_rows_kernel(
+// One workgroup of NT lanes per row.  Two shapes: 1,024 lanes holding 16
+// entries each when the batch has few rows (each row gets a whole CU), 256
+// lanes holding 64 entries each when it has many (several rows per CU, so
+// one row's latency chain overlaps the others').
+template <bool TRANSLATE, int NT, int VPT, int CAP>
+__global__ __launch_bounds__(NT, NT == kManyNT ? 4 : 1) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
     int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, Translate tr) {
-  __shared__ TopkShared<kRowCand> s;
+  __shared__ TopkShared<CAP> s;
   const int r = blockIdx.x;
   const int n = max(0, min(row_len[r], max_len));
   const int m = min(k, n);
-  select_whole_row<kRowNT, kRowVpt, kRowCand, TRANSLATE>(s, scores + (int64_t)r * ld, n, m, k,
-                                                          sel + (int64_t)r * k, sel_count, r, tr);
+  // The many-rows shape is launched only for rows of at most NT*VPT entries.
+  select_whole_row<NT, VPT, CAP, TRANSLATE, NT != kManyNT>(s, scores + (int64_t)r * ld, n, m, k,
+                                                           sel + (int64_t)r * k, sel_count, r, tr);
 }
 
 // Output entries of selection position q (block j of a long-row chunk),
@@ -813,9 +843,12 @@ static int launch_select(const float* scores, int64_t ld, const int32_t* row_len
     if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
     hipLaunchKernelGGL(topk_long_emit_kernel<TRANSLATE>, dim3(num_rows, nchunk), dim3(kLongNT), 0, stream, scores,
                        ld, row_len, max_len, k, sel, sel_count, ws, tr);
+  } else if (num_rows >= kManyMinRows && max_len <= kManyNT * kManyVpt) {
+    hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kManyNT, kManyVpt, kManyCand>), dim3(num_rows), dim3(kManyNT), 0,
+                       stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   } else {
-    hipLaunchKernelGGL(topk_rows_kernel<TRANSLATE>, dim3(num_rows), dim3(kRowNT), 0, stream, scores, ld, row_len,
-                       max_len, k, sel, sel_count, tr);
+    hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kRowNT, kRowVpt, kRowCand>), dim3(num_rows), dim3(kRowNT), 0,
+                       stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   }
   return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
 }

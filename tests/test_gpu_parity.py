@@ -115,6 +115,26 @@ def test_topk_lengths_and_tie_storms(n):
         check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
 
 
+def test_topk_many_rows_exact():
+    # A batch of >= 1,024 rows of at most 16,384 entries takes the many-rows
+    # shape (several rows per CU); mixed lengths, tie storms and rows whose
+    # boundary bin overflows the LDS candidate list.
+    n = 16384
+    R = 1100
+    rng = np.random.default_rng(1100)
+    rows = rng.standard_normal((R, n)).astype(np.float32)
+    rows[:64] = synth.tie_storm_rows(1101, 64, n)
+    rows[64:80] = np.float32(1.0) + rng.integers(0, 3, (16, n)).astype(np.float32) * np.float32(2.0 ** -20)
+    lens = rng.integers(0, n + 1, R).astype(np.int32)
+    special = [0, 1, 511, 512, 513, 2047, 2048, 2049, 16383, 16384]
+    lens[:len(special)] = special
+    lens[64:80] = n
+    for k in (512, 2048):
+        (out,), _ = gu.gpu_topk(rows, lens, k)
+        ref_sel, ref_cnt = oracle.topk(rows, lens, k)
+        check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
+
+
 def test_topk_mixed_lengths_one_launch():
     # one launch mixing every path: take-all, register, streaming, multi-workgroup
     rng = np.random.default_rng(7)
