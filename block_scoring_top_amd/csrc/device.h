@@ -110,12 +110,15 @@ __device__ __forceinline__ uint32_t key32_of(float v) {
 // FP32 -> FP16 with the hardware conversion (round to nearest even, overflow
 // to infinity), then the 16-bit order-preserving key; the coarse bin is its
 // upper 10 bits.
+// After the conversion -0 is folded to +0 by an FP16 add of +0 (round to
+// nearest: -0 + +0 = +0, every other value unchanged).  The key flips all 16
+// bits of a negative pattern and only the sign bit of a non-negative one:
+// b ^ 0x8000 ^ (the sign bit smeared over bits 14..0).
 __device__ __forceinline__ uint32_t bin_of(float v) {
-  _Float16 h = (_Float16)v;
-  uint32_t b = __builtin_bit_cast(uint16_t, h);
-  b = (b == 0x8000u) ? 0u : b;
-  uint32_t key = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
-  return key >> 6;
+  const _Float16 h = (_Float16)v + (_Float16)0.0f;
+  const uint32_t b = __builtin_bit_cast(uint16_t, h);
+  const uint32_t smear = (uint32_t)__builtin_amdgcn_sbfe((int)b, 15, 1) & 0x7FFFu;
+  return ((b ^ smear) ^ 0x8000u) >> 6;
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

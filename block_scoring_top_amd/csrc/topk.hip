@@ -387,7 +387,6 @@ template <int NT, int V, int CAP>
 __device__ __forceinline__ void emit_tile(TopkShared<CAP>& s, float (&x)[V], int base, int n, uint32_t T,
                                           uint32_t& up_pos, uint32_t& cand_pos, int m, int32_t* __restrict__ out,
                                           bool keep) {
-  const int tid = threadIdx.x;
   uint32_t nup = 0, neq = 0;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -444,7 +443,7 @@ template <int NT, int V, int CAP, bool HIST_READY, bool STREAM = true>
 __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m,
                                            int32_t* __restrict__ out, bool keep) {
   constexpr int kTile = V;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
   if (!HIST_READY)
     for (int i = tid; i < kBins; i += NT) s.hist[i] = 0;
   __syncthreads();
@@ -452,22 +451,73 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
   uint32_t T, above;
   const RowReader rd(row, n);
   if (!STREAM || n <= NT * V) {  // !STREAM: the caller guarantees n <= NT*V
+    static_assert(V <= 64, "one mask bit per register entry");
+    // Register path.  The entries' bins are kept, two 16-bit codes per
+    // register (code = bin + 1, 0 past the row), not the FP32 values: after
+    // the threshold, two bit masks mark the entries above and in the
+    // boundary bin, and only the marked entries are visited.  Boundary
+    // entries are re-read by index when their exact keys are needed.
+    uint32_t pb[(V + 1) / 2];
     float x[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) x[i] = rd.at(tid, i * NT);
-    if (!HIST_READY) {
+    for (int i = 0; i < V; ++i) x[i] = rd.at(tid, i * NT);  // every load in flight at once
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        if (i % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // a few bins live at a time
-        if (entry_index<NT>(0, i) < n) atomicAdd(&s.hist[bin_of(x[i])], 1u);
-      }
+    for (int i = 0; i < V; ++i) {
+      if (i % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // a few bins live at a time
+      const bool ok = entry_index<NT>(0, i) < n;
+      const uint32_t b = bin_of(x[i]);
+      if (!HIST_READY && ok) atomicAdd(&s.hist[b], 1u);
+      const uint32_t code = ok ? b + 1u : 0u;
+      pb[i / 2] = (i % 2 == 0) ? code : (pb[i / 2] | (code << 16));
     }
     __syncthreads();
     threshold_to_shared(s, (uint32_t)m);
     T = s.T;
     above = s.above;
-    opaque(x);  // as in emit_tile: no histogram bins kept live
-    emit_tile<NT, V>(s, x, 0, n, T, up_pos, cand_pos, m, out, keep);
+    const uint32_t t1 = T + 1u;
+    uint64_t upm = 0, eqm = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint32_t code = (pb[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+      upm |= (code > t1 ? 1ull : 0ull) << i;
+      eqm |= (code == t1 ? 1ull : 0ull) << i;
+    }
+    const uint32_t nup = (uint32_t)__popcll(upm), neq = (uint32_t)__popcll(eqm);
+    uint32_t total;
+    const uint32_t excl = block_excl_scan<NT>(s, (nup << 20) | neq, total);
+    uint32_t pu = excl >> 20, pe = excl & 0xFFFFFu;
+    while (upm) {
+      const int i = __builtin_ctzll(upm);
+      upm &= upm - 1;
+      if (pu < (uint32_t)m) {
+        const int idx = i * NT + tid;
+        out[pu] = idx;
+        if (keep) s.chosen[pu] = idx;
+      }
+      ++pu;
+    }
+    while (eqm) {
+      const int i = __builtin_ctzll(eqm);
+      eqm &= eqm - 1;
+      if (pe < (uint32_t)CAP) s.cand[pe] = (uint64_t)(uint32_t)(i * NT + tid);  // index only, for now
+      ++pe;
+    }
+    up_pos = total >> 20;
+    cand_pos = total & 0xFFFFFu;
+    __syncthreads();
+    // Exact keys of the listed boundary entries, when a refinement needs them.
+    const uint32_t nc = cand_pos, need = (uint32_t)m - above;
+    if (nc <= (uint32_t)CAP && need < nc) {
+      for (uint32_t j = tid; j < nc; j += NT) {
+        const int idx = (int)(uint32_t)s.cand[j];
+        s.cand[j] = composite_key(rd[idx], idx);
+      }
+    } else if (nc <= (uint32_t)CAP) {
+      for (uint32_t j = tid; j < nc; j += NT) {
+        const int idx = (int)(uint32_t)s.cand[j];
+        s.cand[j] = (uint64_t)inverted_index(idx);  // index_of() reads the low word
+      }
+    }
   } else {
     if (!HIST_READY) {
       for (int b0 = 0; b0 < n; b0 += NT * 8) {
@@ -688,7 +738,7 @@ __global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
     int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
     Translate tr) {
   __shared__ TopkShared<kLongCand> s;
-  const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
+  const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x;
   const int n = max(0, min(row_len[r], max_len));
   if (n < kLongMin) return;
   const int lo = w * kChunk;
