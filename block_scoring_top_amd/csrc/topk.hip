@@ -17,11 +17,14 @@
 //
 // CDNA4 has no thread-block clusters or distributed shared memory.  The
 // blog's paths become:
-//   * many rows (a batch that fills the chip): one 1,024-lane workgroup per
-//     row, the row held in registers (16 values per lane, up to 16,384
-//     entries), longer rows streamed twice;
+//   * rows that are not few-and-long: one workgroup per row, the row held in
+//     registers, 1,024 lanes x 16 values (longer rows streamed twice), or,
+//     for batches of at least 1,024 rows of at most 16,384 entries, 256 lanes
+//     x 64 values so that several rows share a CU.  The register path keeps
+//     each entry's bin, not its value, and marks the entries above and in the
+//     boundary bin with two bit masks;
 //   * few long rows (>= 32,769 entries, at most 256 rows): one 256-lane
-//     workgroup per 4,096-entry chunk (16 entries per lane, in registers).
+//     workgroup per 2,048-entry chunk (8 entries per lane, in registers).
 //     A first launch merges the chunks' LDS histograms into the row's
 //     histogram with device atomics.  In a second launch every chunk finds
 //     the threshold bin, emits and translates its own above-threshold entries
@@ -54,10 +57,10 @@ constexpr int kLongVpt = 16;                   // values per lane held at once t
 constexpr int kLongCand = 4096;
 constexpr int kLongMin = 32769;                // rows this long use several workgroups...
 constexpr int kLongRowsMax = 256;              // ...when the batch has at most this many rows
-constexpr int kChunk = 4096;                   // entries per workgroup on long rows
-constexpr int kPerLane = kChunk / kLongNT;     // 16
+constexpr int kChunk = 2048;                   // entries per workgroup on long rows (a sweep of 1,024-16,384 on 16 x 81,920 rows: 2,048 fastest)
+constexpr int kPerLane = kChunk / kLongNT;     // 8
+constexpr int kChunkPages = 4 * kChunk / kPage;  // logical pages a chunk's blocks span (c <= 4)
 static_assert(kChunk % kLongNT == 0, "a long-row chunk is a whole number of lanes");
-static_assert(4 * kChunk / kPage <= kLongNT, "a chunk's logical pages fit one per lane");
 
 // Workspace record per row (long rows only): merged histogram, counters
 // ([0] arrivals, [1] emitted above the threshold, [2] boundary candidates),
@@ -80,7 +83,7 @@ struct TopkShared {
   uint32_t last;
   uint32_t base_up, base_cand;
   uint64_t red_and[16], red_or[16];
-  int32_t pages[256];  // page ids of a long-row chunk's token range (fused translation)
+  int32_t pages[kChunkPages];  // page ids of a long-row chunk's token range (fused translation)
 };
 
 // Translation context (fused kernels only).
@@ -686,7 +689,7 @@ __device__ __forceinline__ void translate_block_lds(const Translate& tr, int r, 
   }
 }
 
-// Few long rows, first launch: one 256-lane workgroup per 4,096-entry chunk
+// Few long rows, first launch: one 256-lane workgroup per 2,048-entry chunk
 // merges its LDS histogram into the row's histogram with device atomics.
 // Rows shorter than kLongMin are done whole by their first workgroup.
 template <bool TRANSLATE>
@@ -760,11 +763,13 @@ __global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
   RowGeom g{};
   int first_lp = 0;
   if (TRANSLATE) {
-    // The chunk's blocks [lo, lo + kChunk) cover at most 256 logical pages.
+    // The chunk's blocks [lo, lo + kChunk) cover at most kChunkPages logical pages.
     g = row_geometry(tr, r);
     first_lp = (tr.c * lo) >> 6;
-    const int lp = first_lp + tid;
-    s.pages[tid] = lp < tr.pt_stride ? tr.page_table[(int64_t)g.b * tr.pt_stride + lp] : -1;
+    for (int i = tid; i < kChunkPages; i += kLongNT) {
+      const int lp = first_lp + i;
+      s.pages[i] = lp < tr.pt_stride ? tr.page_table[(int64_t)g.b * tr.pt_stride + lp] : -1;
+    }
   }
   __syncthreads();
   threshold_to_shared(s, (uint32_t)m);
