@@ -102,7 +102,7 @@ def cpu_baseline(inp, min_seconds: float):
                       f"{el:.1f} s"}
 
 
-def time_steps(fns, K, warmup, stream, probe=0, probe_every=5):
+def time_steps(fns, K, warmup, stream, probe=0, probe_every=10):
     """Runs the callables of a step K times after `warmup` untimed steps and
     returns (ms per step, avg ms of fns[probe]).
 
