@@ -18,6 +18,21 @@
 //     two more DPP adds sum the heads;
 //   * all rows of a request (up to RG at a time) are scored from the same
 //     key registers, so keys leave HBM once per request.
+//
+// Requests with several rows (speculative verify: 1 accepted + drafts) make
+// the VALU work per key byte grow with the row count; there the rows x keys
+// product goes to the matrix cores instead (score_rows_mfma_kernel):
+//   * v_mfma_f32_16x16x32_bf16 with A = the request's query head-rows (a
+//     row's 4 heads on adjacent M rows, up to 4*NMS rows per pass), B = 16
+//     keys straight from HBM into registers in the B-fragment layout (lane
+//     l reads 16 bytes of key l%16 per k-step: the 64 lanes read the 16 keys'
+//     4 KiB once), no LDS: every wave holds all of the request's rows;
+//   * in the 16x16 accumulator a lane holds the 4 heads of one (row, key):
+//     ReLU, head sum and scale stay in the lane, 16 lanes store 64 contiguous
+//     bytes of a row;
+//   * a 16-key subtile lies in one page, so its page id is wave-uniform (the
+//     chunk's page ids sit one per lane and are read with v_readlane); each
+//     wave keeps P subtiles of loads in flight.
 #include "device.h"
 #include "kernels.h"
 
@@ -143,6 +158,104 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   }
 }
 
+template <int NMS, int P>
+__global__ __launch_bounds__(256) void score_rows_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kcache, int64_t num_pages,
+    const int32_t* __restrict__ page_table, int32_t pt_stride,
+    const int32_t* __restrict__ req_row_ptr, const int32_t* __restrict__ row_pos,
+    int32_t c, int32_t max_vis, int32_t chunk,
+    float* __restrict__ scores, int64_t ld, int32_t* __restrict__ row_len) {
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, i16 = lane & 15;
+  const int r0 = req_row_ptr[b];
+  const int r1 = req_row_ptr[b + 1];
+  if (blockIdx.x == 0 && row_len != nullptr)
+    for (int r = r0 + tid; r < r1; r += blockDim.x) row_len[r] = max(0, min((row_pos[r] + 1) / c, max_vis));
+
+  // The request's longest visible range bounds the chunk.
+  int nmax = 0;
+  for (int r = r0 + lane; r < r1; r += 64) nmax = max(nmax, min((row_pos[r] + 1) / c, max_vis));
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off));
+  nmax = __builtin_amdgcn_readfirstlane(nmax);
+  const int j0 = blockIdx.x * chunk;
+  const int j1 = min(j0 + chunk, nmax);
+  if (j0 >= j1) return;
+  const int per_page = kPage / c;
+  // The chunk spans at most 64 pages: lane i holds the chunk's i-th page id.
+  const int32_t* pt = page_table + (int64_t)b * pt_stride;
+  const int first_page = (c * j0) >> 6;
+  const int npages = ((c * (j1 - 1)) >> 6) - first_page + 1;
+  const int32_t my_page = lane < npages ? pt[first_page + lane] : -1;
+  const int nsub = (j1 - j0 + 15) / 16;
+
+  // B fragment of subtile s (keys j0 + 16*s ..): lane reads key i16 (clamped
+  // to the chunk), dims 32*ks + 8*g .. +7 for ks = 0..3.  valid: the page id
+  // is in range (uniform over the subtile).
+  auto load_sub = [&](int s, u32x4_t(&br)[4], bool& valid) {
+    const int jb = j0 + 16 * s;
+    const int page = __builtin_amdgcn_readlane(my_page, ((c * jb) >> 6) - first_page);
+    valid = page >= 0 && page < num_pages;
+    const int key = min(jb + i16, j1 - 1);
+    const int64_t slot = valid ? (int64_t)page * per_page + (key & (per_page - 1)) : 0;
+    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(kcache + slot * kDim) + g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) br[ks] = __builtin_nontemporal_load(kp + 4 * ks);
+  };
+
+  for (int g0 = r0; g0 < r1; g0 += 4 * NMS) {
+    // A fragments: subtile ms holds rows g0 + 4*ms .. +3, head-row i16 =
+    // 4*(row) + head; k-step ks covers dims 32*ks + 8*g.
+    bf16x8_t afr[NMS][4];
+    int orow[NMS], nv[NMS];
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms) {
+      const int qr = g0 + 4 * ms + (i16 >> 2);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (qr < r1) v = *(reinterpret_cast<const u32x4_t*>(q + ((int64_t)qr * kHeads + (i16 & 3)) * kDim + 32 * ks) + g);
+        afr[ms][ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+      orow[ms] = g0 + 4 * ms + g;  // the accumulator row this lane stores
+      nv[ms] = orow[ms] < r1 ? max(0, min((row_pos[orow[ms]] + 1) / c, max_vis)) : 0;
+    }
+    // This wave's subtiles: wave, wave + 4, ...; P in flight.
+    u32x4_t br[P][4];
+    bool bv[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (wave + 4 * p < nsub) load_sub(wave + 4 * p, br[p], bv[p]);
+    for (int s0 = wave; s0 < nsub; s0 += 4 * P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int s = s0 + 4 * p;
+        if (s < nsub) {
+          f32x4_t acc[NMS];
+          const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms)
+              acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], __builtin_bit_cast(bf16x8_t, br[p][ks]),
+                                                                ks == 0 ? zero : acc[ms], 0, 0, 0);
+          const bool ok = bv[p];
+          if (s + 4 * P < nsub) load_sub(s + 4 * P, br[p], bv[p]);  // refill this slot
+          const int j = j0 + 16 * s + i16;
+#pragma unroll
+          for (int ms = 0; ms < NMS; ++ms) {
+            const f32x4_t a = acc[ms];
+            const float sc = ((fmaxf(a.x, 0.f) + fmaxf(a.y, 0.f)) + (fmaxf(a.z, 0.f) + fmaxf(a.w, 0.f))) * kScale;
+            if (j < j1 && j < nv[ms]) scores[(int64_t)orow[ms] * ld + j] = ok ? sc : __builtin_nanf("");
+          }
+        }
+      }
+    }
+  }
+}
+
 static int pick_rg(int num_rows, int num_req) {
   const int avg = (num_rows + num_req - 1) / num_req;
   return avg <= 1 ? 1 : avg <= 2 ? 2 : avg <= 4 ? 4 : 8;
@@ -163,6 +276,23 @@ int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_p
   const int nchunks = max_vis > 0 ? (int)((max_vis + chunk - 1) / chunk) : 1;
   dim3 grid(nchunks, num_req), block(256);
   const int rg = pick_rg(num_rows, num_req);
+  if (rg >= 4) {
+    // Several rows per request: the matrix-core kernel, 256-key chunks.
+    constexpr int kChunkM = 256, P = 2;
+    const int nch = max_vis > 0 ? (max_vis + kChunkM - 1) / kChunkM : 1;
+    const int avg = (num_rows + num_req - 1) / num_req;
+    dim3 gm(nch, num_req);
+    if (avg <= 4)
+      hipLaunchKernelGGL((score_rows_mfma_kernel<1, P>), gm, block, 0, stream, q, kcache, num_pages, page_table,
+                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
+    else if (avg <= 8)
+      hipLaunchKernelGGL((score_rows_mfma_kernel<2, P>), gm, block, 0, stream, q, kcache, num_pages, page_table,
+                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
+    else
+      hipLaunchKernelGGL((score_rows_mfma_kernel<4, P>), gm, block, 0, stream, q, kcache, num_pages, page_table,
+                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
+    return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
+  }
 #define BS_LAUNCH_DECODE(RGV)                                                                 \
   hipLaunchKernelGGL((score_decode_kernel<RGV, U>), grid, block, 0, stream, q, kcache, num_pages, \
                      page_table, pt_stride, req_row_ptr, row_pos, c, max_vis, (int32_t)chunk,    \

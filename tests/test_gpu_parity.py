@@ -72,6 +72,18 @@ def test_decode_edge_rows():
     _full_check(inp1)
 
 
+@pytest.mark.parametrize("c", [4, 1])
+def test_decode_many_rows_per_request(c):
+    # 11 rows per request on average: the matrix-core multi-row scorer with
+    # 16 rows per pass (a 20-row request takes two passes); a 1-row request
+    # and rows near page boundaries in the same batch.
+    rng = np.random.default_rng(303 + c)
+    rows = [list(range(2000, 2020)), [63], list(range(4090, 4103)), list(range(900, 911))]
+    inp = synth.build_paged_batch("many", 303 + c, c=c, k=64, ctx_tokens=[2020, 64, 4103, 911],
+                                  row_pos_per_req=rows, rng=rng)
+    _full_check(inp)
+
+
 def test_decode_power_of_two_scaling_exact():
     # s(2q) == 2*s(q) bit for bit in any fixed accumulation order.
     inp = synth.qsa_verify_64req(B=4, lo=1000, hi=9000)
