@@ -607,10 +607,20 @@ __device__ __forceinline__ void put_slot(const Translate& tr, const RowGeom& g, 
   if (tr.out_pos) tr.out_pos[(int64_t)r * tr.ld_out + i] = pos;
 }
 
-// Output entries of selection position q (block j).
+// Output entries of selection position q (block j): the block's c positions
+// lie in one page, so one page-table read serves them all.
 __device__ __forceinline__ void translate_block(const Translate& tr, const RowGeom& g, int r, int q, int j) {
   const int c = tr.c;
-  for (int u = 0; u < c; ++u) put_slot(tr, g, r, q * c + u, (j >= 0 && j < g.nv) ? c * j + u : -1);
+  const bool valid = j >= 0 && j < g.nv;
+  const int p0 = c * j;
+  int page = -1;
+  if (valid && (p0 >> 6) < tr.pt_stride) page = tr.page_table[(int64_t)g.b * tr.pt_stride + (p0 >> 6)];
+  int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out + q * c;
+  int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out + q * c : nullptr;
+  for (int u = 0; u < c; ++u) {
+    orow[u] = page >= 0 ? page * kPage + ((p0 + u) & (kPage - 1)) : -1;
+    if (prow) prow[u] = valid ? p0 + u : -1;
+  }
 }
 
 // Output entries from m*c on: the pending tail, then -1; and the count.
@@ -627,9 +637,37 @@ template <int NT>
 __device__ __forceinline__ void translate_row(const Translate& tr, int r, int m, const int32_t* chosen) {
   const RowGeom g = row_geometry(tr, r);
   const int c = tr.c;
-  for (int i = threadIdx.x; i < c * m; i += NT) {
-    const int q = i / c, j = chosen[q];
-    put_slot(tr, g, r, i, (j >= 0 && j < g.nv) ? c * j + (i - q * c) : -1);
+  // Each lane's selection positions: their page ids are read first, all in
+  // flight together (one read per block), then the c slots of each block are
+  // written.
+  constexpr int PB = (kKmax + NT - 1) / NT;
+  const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
+  int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out;
+  int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out : nullptr;
+  int pos0[PB], page[PB];
+#pragma unroll
+  for (int t = 0; t < PB; ++t) {
+    const int q = (int)threadIdx.x + t * NT;
+    int p0 = -1, pg = -1;
+    if (q < m) {
+      const int j = chosen[q];
+      if (j >= 0 && j < g.nv) {
+        p0 = c * j;
+        if ((p0 >> 6) < tr.pt_stride) pg = pt[p0 >> 6];
+      }
+    }
+    pos0[t] = p0;
+    page[t] = pg;
+  }
+#pragma unroll
+  for (int t = 0; t < PB; ++t) {
+    const int q = (int)threadIdx.x + t * NT;
+    if (q < m) {
+      for (int u = 0; u < c; ++u) {
+        orow[q * c + u] = page[t] >= 0 ? page[t] * kPage + ((pos0[t] + u) & (kPage - 1)) : -1;
+        if (prow) prow[q * c + u] = pos0[t] >= 0 ? pos0[t] + u : -1;
+      }
+    }
   }
   translate_tail<NT>(tr, g, r, m);
 }
