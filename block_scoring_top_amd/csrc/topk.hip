@@ -38,8 +38,8 @@
 //     loads and stores, performed at the device coherence point; each chunk
 //     waits for its stores to complete before it arrives;
 //   * emission is count, block scan, write (no per-entry atomics); the
-//     threshold scans and the boundary refinement run on one wave,
-//     wave-synchronously, with DPP scans (no block barriers inside).
+//     threshold scan runs on one wave with DPP scans; the boundary
+//     refinement costs one workgroup barrier per 8-bit radix pass.
 #include "device.h"
 #include "kernels.h"
 
@@ -200,17 +200,39 @@ __device__ __forceinline__ uint32_t block_excl_scan(TopkShared<CAP>& s, uint32_t
   return off + incl - x;
 }
 
+// Translation of the refinement's winners as they are emitted: a winner at
+// selection position q holding block j fills output entries q*c .. q*c+c-1
+// (positions c*j + u, slots page*64 + (c*j + u) mod 64, page read from the
+// request's page-table row; -1 for an invalid block or page).  pt == nullptr:
+// no translation.
+struct WinnerTr {
+  const int32_t* pt;
+  int c, nv, pt_stride;
+  int32_t* orow;
+  int32_t* prow;  // may be nullptr
+};
+
 // The whole workgroup resolves the boundary bin from s.cand[0..nc) (nc > need
-// >= 1, nc <= CAP): each lane holds up to CAP/NT candidates in registers;
-// per 8-bit digit (after the bits all candidates share) every lane adds its
-// matching candidates to an LDS digit histogram, wave 0 finds the digit, all
-// lanes narrow the prefix.  The `need` winners are emitted by count, block
-// scan, write at out[base ...] (and chosen[base ...]).
+// >= 1, nc <= CAP): each lane holds up to PER candidates in registers
+// (candidate i*NT + lane).  An exact MSB-first radix selection on the 64-bit
+// keys, 8-bit digits after the bits all candidates share: per pass every lane
+// adds its matching candidates to an LDS digit histogram, one barrier, then
+// every wave finds the same digit from that histogram by itself.  Three digit
+// buffers rotate (in s.hist, free once the threshold bin is known), so one
+// barrier per pass suffices: the buffer pass p + 1 fills was last read in
+// pass p - 2 and is cleared during pass p.  The `need` winners are
+// emitted by count, block scan, write at out[base ...] (and chosen[base ...]);
+// with translation each lane reads the page ids of its own candidates before
+// the passes and writes the winners' slots as it emits them.
 template <int NT, int CAP, int PER>
 __device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc, uint32_t need,
-                                                 int32_t* __restrict__ out, int32_t* chosen, uint32_t base, int limit) {
+                                                 int32_t* __restrict__ out, int32_t* chosen, uint32_t base, int limit,
+                                                 const WinnerTr& wt) {
+  static_assert(3 * 256 <= kBins, "three digit buffers fit in the histogram's storage");
   const int tid = threadIdx.x, wave = tid >> 6;
+  uint32_t* const dig = s.hist;
   uint64_t key[PER];
+  int pg[PER];
   uint64_t a = ~0ull, o = 0ull;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -221,12 +243,22 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc
       o |= key[i];
     }
   }
+  if (wt.pt) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = index_of(key[i]);
+      const int p0 = wt.c * idx;
+      pg[i] = -1;
+      if ((uint32_t)(i * NT + tid) < nc && idx >= 0 && idx < wt.nv && (p0 >> 6) < wt.pt_stride) pg[i] = wt.pt[p0 >> 6];
+    }
+  }
   a = wave_and64(a);
   o = wave_or64(o);
   if (lane_id() == 0) {
     s.red_and[wave] = a;
     s.red_or[wave] = o;
   }
+  for (int i = tid; i < 512; i += NT) dig[i] = 0;  // buffers 0 and 1
   __syncthreads();
   a = ~0ull;
   o = 0ull;
@@ -240,33 +272,27 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc
   uint64_t mask = ~((2ull << hb) - 1ull);
   uint64_t prefix = o & mask;
   uint32_t remaining = need;
-  for (;;) {
+  for (int pass = 0;; ++pass) {
     const int width = hb + 1 < 8 ? hb + 1 : 8;
     const int shift = hb + 1 - width;
     const int nb = 1 << width;
-    for (int i = tid; i < 256; i += NT) s.digit[i] = 0;  // bins past nb stay 0
-    __syncthreads();
+    uint32_t* const cur = dig + 256 * (pass % 3);
+    // The buffer the next pass fills was last read in pass - 2, before the
+    // previous barrier; buffers 0 and 1 start cleared.
+    uint32_t* const next = dig + 256 * ((pass + 1) % 3);
+    if (pass >= 1)
+      for (int i = tid; i < 256; i += NT) next[i] = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
       if ((uint32_t)(i * NT + tid) < nc && (key[i] & mask) == prefix)
-        atomicAdd(&s.digit[(key[i] >> shift) & (uint64_t)(nb - 1)], 1u);
+        atomicAdd(&cur[(key[i] >> shift) & (uint64_t)(nb - 1)], 1u);
     __syncthreads();
-    if (wave == 0) {
-      uint32_t d, ab;
-      wave_threshold<256>(s.digit, remaining, d, ab);
-      if (lane_id() == 0) {
-        s.T = d;
-        s.above = ab;
-      }
-    }
-    __syncthreads();
-    const uint32_t d = s.T;
-    remaining -= s.above;
+    uint32_t d, ab;
+    wave_threshold<256>(cur, remaining, d, ab);
+    remaining -= ab;
     prefix |= (uint64_t)d << shift;
     mask |= (uint64_t)(nb - 1) << shift;
-    const bool settled = s.digit[d] == remaining;
-    __syncthreads();
-    if (settled || shift == 0) break;
+    if (cur[d] == remaining || shift == 0) break;
     hb = shift - 1;
   }
   uint32_t cnt = 0;
@@ -281,20 +307,30 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc
         const int idx = index_of(key[i]);
         out[pos] = idx;
         if (chosen) chosen[pos] = idx;
+        if (wt.pt) {
+          const bool valid = idx >= 0 && idx < wt.nv;
+          const int p0 = wt.c * idx;
+          for (int u = 0; u < wt.c; ++u) {
+            wt.orow[pos * wt.c + u] = pg[i] >= 0 ? pg[i] * kPage + ((p0 + u) & (kPage - 1)) : -1;
+            if (wt.prow) wt.prow[pos * wt.c + u] = valid ? p0 + u : -1;
+          }
+        }
       }
       ++pos;
     }
   }
 }
 
-// Holds just as many candidates per lane as nc needs.
+// Holds just as many candidates per lane as nc needs.  All lanes call.
 template <int NT, int CAP>
 __device__ __forceinline__ void block_refine(TopkShared<CAP>& s, uint32_t nc, uint32_t need, int32_t* __restrict__ out,
-                                             int32_t* chosen, uint32_t base, int limit) {
+                                             int32_t* chosen, uint32_t base, int limit,
+                                             const WinnerTr& wt = WinnerTr{}) {
   constexpr int PMAX = (CAP + NT - 1) / NT;
-  if (PMAX > 2 && nc <= 2u * NT) block_refine_per<NT, CAP, 2>(s, nc, need, out, chosen, base, limit);
-  else if (PMAX > 4 && nc <= 4u * NT) block_refine_per<NT, CAP, 4>(s, nc, need, out, chosen, base, limit);
-  else block_refine_per<NT, CAP, PMAX>(s, nc, need, out, chosen, base, limit);
+  if (PMAX > 1 && nc <= (uint32_t)NT) block_refine_per<NT, CAP, 1>(s, nc, need, out, chosen, base, limit, wt);
+  else if (PMAX > 2 && nc <= 2u * NT) block_refine_per<NT, CAP, 2>(s, nc, need, out, chosen, base, limit, wt);
+  else if (PMAX > 4 && nc <= 4u * NT) block_refine_per<NT, CAP, 4>(s, nc, need, out, chosen, base, limit, wt);
+  else block_refine_per<NT, CAP, PMAX>(s, nc, need, out, chosen, base, limit, wt);
 }
 
 // Block-wide fallback when the boundary bin overflows the LDS list: radix
@@ -875,13 +911,26 @@ __global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
   __syncthreads();
   if (!s.last) return;
 
-  // The last chunk to arrive resolves the boundary bin.
+  // The last chunk to arrive resolves the boundary bin.  The head of the
+  // candidate list is read together with its length (one round trip); the
+  // list's storage holds kLongCand entries, those past the length are unused.
+  constexpr int kSpec = 4;
+  static_assert(kSpec * kLongNT <= kLongCand, "speculative reads stay inside the list");
+  uint64_t head[kSpec];
+#pragma unroll
+  for (int t = 0; t < kSpec; ++t)
+    head[t] = __hip_atomic_load(&gcand[t * kLongNT + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t nc = __hip_atomic_load(&ctr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t need = (uint32_t)m - above;
-  if (nc <= (uint32_t)kLongCand)
-    for (int i = tid; i < (int)nc; i += kLongNT)
+  if (nc <= (uint32_t)kLongCand) {
+#pragma unroll
+    for (int t = 0; t < kSpec; ++t)
+      if ((uint32_t)(t * kLongNT + tid) < nc) s.cand[t * kLongNT + tid] = head[t];
+    for (int i = kSpec * kLongNT + tid; i < (int)nc; i += kLongNT)
       s.cand[i] = __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
+  bool translated = false;
   if (need >= 1 && need <= (uint32_t)m) {
     if (nc <= (uint32_t)kLongCand) {
       if (need >= nc) {
@@ -894,7 +943,13 @@ __global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
           }
         }
       } else {
-        block_refine<kLongNT, kLongCand>(s, nc, need, out, s.chosen, above, m);
+        WinnerTr wt{};
+        if (TRANSLATE)
+          wt = WinnerTr{tr.page_table + (int64_t)g.b * tr.pt_stride, tr.c, g.nv, tr.pt_stride,
+                        tr.out_slots + (int64_t)r * tr.ld_out,
+                        tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out : nullptr};
+        block_refine<kLongNT, kLongCand>(s, nc, need, out, s.chosen, above, m, wt);
+        translated = TRANSLATE;
       }
       __syncthreads();
     } else {
@@ -905,7 +960,8 @@ __global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
   }
   if (tid == 0) sel_count[r] = m;
   if (TRANSLATE) {
-    for (int q = (int)above + tid; q < m; q += kLongNT) translate_block(tr, g, r, q, s.chosen[q]);
+    if (!translated)
+      for (int q = (int)above + tid; q < m; q += kLongNT) translate_block(tr, g, r, q, s.chosen[q]);
     translate_tail<kLongNT>(tr, g, r, m);
   }
   // Leave the row's workspace zero-filled for the next call.
