@@ -121,6 +121,30 @@ __device__ __forceinline__ uint32_t bin_of(float v) {
   return ((b ^ smear) ^ 0x8000u) >> 6;
 }
 
+// bin_of for two values at once (the same mapping, entry a in the low 16
+// bits of the result, b in the high 16): one packed FP32 -> FP16 conversion
+// (round to nearest even), one packed FP16 add of +0, and the key transform
+// on both 16-bit halves.
+typedef _Float16 bs_half2 __attribute__((ext_vector_type(2)));
+typedef float bs_float2 __attribute__((ext_vector_type(2)));
+typedef uint16_t bs_ushort2 __attribute__((ext_vector_type(2)));
+typedef int16_t bs_short2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bin_pair(float a, float b) {
+  const bs_half2 h = __builtin_convertvector((bs_float2){a, b}, bs_half2) + (bs_half2){0, 0};
+  const bs_ushort2 u = __builtin_bit_cast(bs_ushort2, h);
+  const bs_short2 sign = __builtin_bit_cast(bs_short2, u) >> 15;
+  const bs_ushort2 key = u ^ (__builtin_bit_cast(bs_ushort2, sign) | (bs_ushort2){0x8000, 0x8000});
+  return __builtin_bit_cast(uint32_t, (bs_ushort2)(key >> 6));
+}
+
+// Per 16-bit half: 1 if the half of `codes` exceeds the same half of `t`,
+// else 0 (a saturating packed subtract, then a packed min with 1).
+__device__ __forceinline__ uint32_t pk_gt_flags(uint32_t codes, uint32_t t) {
+  uint32_t g;
+  asm("v_pk_sub_u16 %0, %1, %2 clamp\n\tv_pk_min_u16 %0, %0, 1 op_sel_hi:[1,0]" : "=&v"(g) : "v"(codes), "v"(t));
+  return g;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Reads FP32 entries of one row through a raw buffer resource: one lane

@@ -496,30 +496,58 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
     // the threshold, two bit masks mark the entries above and in the
     // boundary bin, and only the marked entries are visited.  Boundary
     // entries are re-read by index when their exact keys are needed.
-    uint32_t pb[(V + 1) / 2];
+    // Entries are handled in pairs (x[2p], x[2p+1]) with packed 16-bit
+    // arithmetic: two bins per conversion, and a pair is checked against
+    // the row length once for the whole workgroup unless it straddles the
+    // row's end.
+    static_assert(V % 2 == 0, "entries are binned in pairs");
+    constexpr int P = V / 2;
+    uint32_t pb[P];
     float x[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) x[i] = rd.at(tid, i * NT);  // every load in flight at once
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      if (i % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // a few bins live at a time
-      const bool ok = entry_index<NT>(0, i) < n;
-      const uint32_t b = bin_of(x[i]);
-      if (!HIST_READY && ok) atomicAdd(&s.hist[b], 1u);
-      const uint32_t code = ok ? b + 1u : 0u;
-      pb[i / 2] = (i % 2 == 0) ? code : (pb[i / 2] | (code << 16));
+    for (int p = 0; p < P; ++p) {
+      if (p % 4 == 0) __builtin_amdgcn_sched_barrier(0);  // a few bins live at a time
+      const uint32_t B = bin_pair(x[2 * p], x[2 * p + 1]);
+      uint32_t code;
+      if ((2 * p + 2) * NT <= n) {  // the whole pair lies inside the row, for every lane
+        if (!HIST_READY) {
+          atomicAdd(&s.hist[B & 0xFFFFu], 1u);
+          atomicAdd(&s.hist[B >> 16], 1u);
+        }
+        code = B + 0x00010001u;
+      } else {
+        const bool ok0 = entry_index<NT>(0, 2 * p) < n, ok1 = entry_index<NT>(0, 2 * p + 1) < n;
+        if (!HIST_READY && ok0) atomicAdd(&s.hist[B & 0xFFFFu], 1u);
+        if (!HIST_READY && ok1) atomicAdd(&s.hist[B >> 16], 1u);
+        code = (ok0 ? (B & 0xFFFFu) + 1u : 0u) | (ok1 ? (B & 0xFFFF0000u) + 0x00010000u : 0u);
+      }
+      asm volatile("" : "+v"(code));  // packed here, not sunk past the loop
+      pb[p] = code;
     }
     __syncthreads();
     threshold_to_shared(s, (uint32_t)m);
     T = s.T;
     above = s.above;
-    const uint32_t t1 = T + 1u;
+    // Bit i of upm / eqm: entry i's code (bin + 1) above / equal to T + 1.
+    // Per pair, the 0/1 flags of both halves are placed by one dot product
+    // with the halves' bit weights, 16 bits (8 pairs) per word.
+    const uint32_t tgt = (T + 1u) * 0x00010001u, tge = T * 0x00010001u;
+    uint32_t upw[(P + 7) / 8], gew[(P + 7) / 8];
+#pragma unroll
+    for (int w = 0; w < (P + 7) / 8; ++w) upw[w] = gew[w] = 0u;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const bs_ushort2 wt = {(uint16_t)(1u << (2 * (p % 8))), (uint16_t)(2u << (2 * (p % 8)))};
+      upw[p / 8] = __builtin_amdgcn_udot2(__builtin_bit_cast(bs_ushort2, pk_gt_flags(pb[p], tgt)), wt, upw[p / 8], false);
+      gew[p / 8] = __builtin_amdgcn_udot2(__builtin_bit_cast(bs_ushort2, pk_gt_flags(pb[p], tge)), wt, gew[p / 8], false);
+    }
     uint64_t upm = 0, eqm = 0;
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const uint32_t code = (pb[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
-      upm |= (code > t1 ? 1ull : 0ull) << i;
-      eqm |= (code == t1 ? 1ull : 0ull) << i;
+    for (int w = 0; w < (P + 7) / 8; ++w) {
+      upm |= (uint64_t)upw[w] << (16 * w);
+      eqm |= (uint64_t)(gew[w] & ~upw[w]) << (16 * w);
     }
     const uint32_t nup = (uint32_t)__popcll(upm), neq = (uint32_t)__popcll(eqm);
     uint32_t total;
