@@ -661,6 +661,33 @@ __device__ __forceinline__ RowGeom row_geometry(const Translate& tr, int r) {
   return g;
 }
 
+// The same, split so that its reads can be issued long before the values
+// are needed: start() reads the row's position and the first 64 request
+// starts (one per lane), finish() turns them into the geometry (all 64
+// lanes of each wave call both; requests past the first 64 are read there).
+struct RowGeomReads {
+  int t, start;
+};
+
+__device__ __forceinline__ RowGeomReads row_geometry_start(const Translate& tr, int r) {
+  const int bi = lane_id();
+  return RowGeomReads{tr.row_pos[r], bi < tr.num_req ? tr.req_row_ptr[bi] : 0x7FFFFFFF};
+}
+
+__device__ __forceinline__ RowGeom row_geometry_finish(const Translate& tr, int r, const RowGeomReads& rd) {
+  int b = __popcll(__ballot(rd.start <= r)) - 1;
+  for (int base = 64; base < tr.num_req; base += 64) {
+    const int bi = base + lane_id();
+    b += __popcll(__ballot(bi < tr.num_req && tr.req_row_ptr[bi] <= r));
+  }
+  RowGeom g;
+  g.b = max(0, min(b, tr.num_req - 1));
+  g.t = rd.t;
+  g.nv = g.t >= 0 ? (g.t + 1) / tr.c : 0;
+  g.p = g.t >= 0 ? g.t + 1 - tr.c * g.nv : 0;
+  return g;
+}
+
 __device__ __forceinline__ void put_slot(const Translate& tr, const RowGeom& g, int r, int i, int pos) {
   int slot = -1;
   if (pos >= 0 && (pos >> 6) < tr.pt_stride) {
@@ -695,45 +722,47 @@ __device__ __forceinline__ void translate_tail(const Translate& tr, const RowGeo
   if (threadIdx.x == 0) tr.out_count[r] = total;
 }
 
-// The whole row from chosen[0..m).  All lanes call (request lookup uses
-// whole waves).
+// The whole row from chosen[0..m).  Element-major: lane l handles output
+// entries l, l + NT, l + 2*NT, ..., so every store instruction of a wave
+// covers 256 contiguous bytes; entry i < c*m belongs to selection position
+// i / c (c is 1 or 4), entries from c*m on are the pending tail, then -1.
+// Each round reads the page ids of its E entries per lane first (the c
+// entries of a block share one address), then writes them.
 template <int NT>
-__device__ __forceinline__ void translate_row(const Translate& tr, int r, int m, const int32_t* chosen) {
-  const RowGeom g = row_geometry(tr, r);
-  const int c = tr.c;
-  // Each lane's selection positions: their page ids are read first, all in
-  // flight together (one read per block), then the c slots of each block are
-  // written.
-  constexpr int PB = (kKmax + NT - 1) / NT;
+__device__ __forceinline__ void translate_row(const Translate& tr, const RowGeom& g, int r, int m,
+                                              const int32_t* chosen) {
+  constexpr int E = 8;
+  const int c = tr.c, sh = c == 4 ? 2 : 0;
+  const int nblk = c * m, total = nblk + g.p;
   const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
   int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out;
   int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out : nullptr;
-  int pos0[PB], page[PB];
+  for (int i0 = 0; i0 < tr.ld_out; i0 += E * NT) {
+    int pos[E], page[E];
 #pragma unroll
-  for (int t = 0; t < PB; ++t) {
-    const int q = (int)threadIdx.x + t * NT;
-    int p0 = -1, pg = -1;
-    if (q < m) {
-      const int j = chosen[q];
-      if (j >= 0 && j < g.nv) {
-        p0 = c * j;
-        if ((p0 >> 6) < tr.pt_stride) pg = pt[p0 >> 6];
+    for (int e = 0; e < E; ++e) {
+      const int i = i0 + e * NT + (int)threadIdx.x;
+      int ps = -1, pg = -1;
+      if (i < nblk) {
+        const int j = chosen[i >> sh];
+        if (j >= 0 && j < g.nv) ps = c * j + (i & (c - 1));
+      } else if (i < total) {
+        ps = c * g.nv + (i - nblk);
+      }
+      if (ps >= 0 && (ps >> 6) < tr.pt_stride) pg = pt[ps >> 6];
+      pos[e] = ps;
+      page[e] = pg;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = i0 + e * NT + (int)threadIdx.x;
+      if (i < tr.ld_out) {
+        orow[i] = page[e] >= 0 ? page[e] * kPage + (pos[e] & (kPage - 1)) : -1;
+        if (prow) prow[i] = pos[e];
       }
     }
-    pos0[t] = p0;
-    page[t] = pg;
   }
-#pragma unroll
-  for (int t = 0; t < PB; ++t) {
-    const int q = (int)threadIdx.x + t * NT;
-    if (q < m) {
-      for (int u = 0; u < c; ++u) {
-        orow[q * c + u] = page[t] >= 0 ? page[t] * kPage + ((pos0[t] + u) & (kPage - 1)) : -1;
-        if (prow) prow[q * c + u] = pos0[t] >= 0 ? pos0[t] + u : -1;
-      }
-    }
-  }
-  translate_tail<NT>(tr, g, r, m);
+  if (threadIdx.x == 0) tr.out_count[r] = total;
 }
 
 // The whole selection of one row by one workgroup, any n.
@@ -742,6 +771,8 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float
                                  int32_t* __restrict__ out, int32_t* __restrict__ sel_count, int r,
                                  const Translate& tr) {
   const int tid = threadIdx.x;
+  RowGeomReads gr{};
+  if (TRANSLATE) gr = row_geometry_start(tr, r);  // in flight during the selection
   for (int i = m + tid; i < k; i += NT) out[i] = -1;
   if (tid == 0) sel_count[r] = m;
   if (m == n) {
@@ -754,7 +785,7 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float
   }
   if (TRANSLATE) {
     __syncthreads();
-    translate_row<NT>(tr, r, m, s.chosen);
+    translate_row<NT>(tr, row_geometry_finish(tr, r, gr), r, m, s.chosen);
   }
 }
 
