@@ -141,21 +141,10 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
     int b = 0, rb0 = 0, rb1 = 0;
     if (!pf_locate(bi, req_row_ptr, num_req, b, rb0, rb1)) break;  // past the last block
 
-    // Visible lengths: the block's longest bounds its tiles; the wave's
-    // shortest decides which tiles store without masks.
-    int nmax = 0;
-    if (lane < rb1 - rb0) nmax = max(0, min((row_pos[rb0 + lane] + 1) / c, max_vis));
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off));
-    nmax = __builtin_amdgcn_readfirstlane(nmax);
-    const int t0 = tb;
-    const int t1 = min(te_range, (nmax + kPfKeys - 1) / kPfKeys);
-    if (t0 >= t1) continue;
-
     // A fragments: M-subtile ms covers query rows 4*ms .. 4*ms+3 of this
     // wave, head-row i16 = 4*(row) + head; k-step ks covers dims 32*ks + 8*g.
+    // All 16 reads are issued before anything waits on memory.
     bf16x8_t afr[4][4];
-    int nvis[4];
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
       const int qr = rb0 + wave * 16 + ms * 4 + (i16 >> 2);
@@ -167,9 +156,22 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
         if (ok) v = *(reinterpret_cast<const u32x4_t*>(q + ((int64_t)qr * kHeads + head) * kDim + 32 * ks) + g);
         afr[ms][ks] = __builtin_bit_cast(bf16x8_t, v);
       }
-      const int orow = rb0 + wave * 16 + ms * 4 + g;  // the accumulator row this lane stores
-      nvis[ms] = orow < rb1 ? max(0, min((row_pos[orow] + 1) / c, max_vis)) : 0;
     }
+    // Visible lengths, one read per row of the block (lane L: row rb0 + L,
+    // 0 past the block): the block's longest bounds its tiles; each lane
+    // takes those of the 4 rows it stores by shuffle; the wave's shortest
+    // decides which tiles store without masks.
+    const int nv_lane = lane < rb1 - rb0 ? max(0, min((row_pos[rb0 + lane] + 1) / c, max_vis)) : 0;
+    int nmax = nv_lane;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off));
+    nmax = __builtin_amdgcn_readfirstlane(nmax);
+    const int t0 = tb;
+    const int t1 = min(te_range, (nmax + kPfKeys - 1) / kPfKeys);
+    if (t0 >= t1) continue;
+    int nvis[4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) nvis[ms] = __shfl(nv_lane, wave * 16 + ms * 4 + g);  // row stored by this lane
     int wmin = min(min(nvis[0], nvis[1]), min(nvis[2], nvis[3]));
     wmin = min(wmin, __shfl_xor(wmin, 16));
     wmin = min(wmin, __shfl_xor(wmin, 32));
@@ -261,10 +263,19 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
     for (int t = t0; t < t1; ++t) {
       const int i = t - t0;
       dma_group(t + 2, page_ahead, (i + 2) % kPfBufs);
-      page_ahead = group_page(t + 3);
       f32x4_t acc[4][4], v[4];
       mfma_tile(acc, i % kPfBufs);
+      // Scheduling fences keep the order: the tile's MFMAs, then the next
+      // page id (a scalar read issued earlier would make the fragment-read
+      // waits above wait for it too), then the epilogue, and only then the
+      // wait for tile t+1, which also waits for the previous tile's stores
+      // (vector memory operations retire in issue order).
+      __builtin_amdgcn_sched_barrier(0);
+      page_ahead = group_page(t + 3);
       head_sums(acc, v);
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) asm volatile("" : "+v"(v[ms]));  // computed here, not in the store branches
+      __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<4>();  // tile t+1 is in LDS (and every older store is done)
       store_tile(v, t);
       barrier_lds();

@@ -59,6 +59,9 @@ constexpr int kLongMin = 32769;                // rows this long use several wor
 constexpr int kLongRowsMax = 256;              // ...when the batch has at most this many rows
 constexpr int kChunk = 2048;                   // entries per workgroup on long rows (a sweep of 1,024-16,384 on 16 x 81,920 rows: 2,048 fastest)
 constexpr int kPerLane = kChunk / kLongNT;     // 8
+constexpr int kHistChunk = 4096;               // entries per workgroup in the long-row histogram launch (2,048-8,192 measured alike)
+constexpr int kHistPerLane = kHistChunk / kLongNT;
+static_assert(kHistChunk % (2 * kLongNT) == 0, "histogram chunks are whole lane pairs");
 constexpr int kChunkPages = 4 * kChunk / kPage;  // logical pages a chunk's blocks span (c <= 4)
 static_assert(kChunk % kLongNT == 0, "a long-row chunk is a whole number of lanes");
 
@@ -822,7 +825,7 @@ __device__ __forceinline__ void translate_block_lds(const Translate& tr, int r, 
   }
 }
 
-// Few long rows, first launch: one 256-lane workgroup per 2,048-entry chunk
+// Few long rows, first launch: one 256-lane workgroup per 4,096-entry chunk
 // merges its LDS histogram into the row's histogram with device atomics.
 // Rows shorter than kLongMin are done whole by their first workgroup.
 template <bool TRANSLATE>
@@ -841,18 +844,26 @@ __global__ __launch_bounds__(kLongNT) void topk_long_hist_kernel(
                                                                  r, tr);
     return;
   }
-  const int lo = w * kChunk;
+  const int lo = w * kHistChunk;
   if (lo >= n) return;
   uint32_t* gh = reinterpret_cast<uint32_t*>(ws + (size_t)r * kWsRow + kWsHist);
   for (int i = tid; i < kBins; i += kLongNT) s.hist[i] = 0;
-  __syncthreads();
   const RowReader rd(row, n);
-  float x[kPerLane];
+  float x[kHistPerLane];
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) x[i] = rd[lo + i * kLongNT + tid];
+  for (int i = 0; i < kHistPerLane; ++i) x[i] = rd.at(tid, lo + i * kLongNT);
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i)
-    if (lo + i * kLongNT + tid < n) atomicAdd(&s.hist[bin_of(x[i])], 1u);
+  for (int p = 0; p < kHistPerLane / 2; ++p) {
+    const uint32_t B = bin_pair(x[2 * p], x[2 * p + 1]);
+    if (lo + (2 * p + 2) * kLongNT <= n) {  // both entries inside the row, for every lane
+      atomicAdd(&s.hist[B & 0xFFFFu], 1u);
+      atomicAdd(&s.hist[B >> 16], 1u);
+    } else {
+      if (lo + 2 * p * kLongNT + tid < n) atomicAdd(&s.hist[B & 0xFFFFu], 1u);
+      if (lo + (2 * p + 1) * kLongNT + tid < n) atomicAdd(&s.hist[B >> 16], 1u);
+    }
+  }
   __syncthreads();
   for (int i = tid; i < kBins; i += kLongNT) {
     const uint32_t cnt = s.hist[i];
@@ -1045,8 +1056,9 @@ static int launch_select(const float* scores, int64_t ld, const int32_t* row_len
                          hipStream_t stream) {
   if (use_long_path(num_rows, max_len)) {
     const int nchunk = (max_len + kChunk - 1) / kChunk;
+    const int nhist = (max_len + kHistChunk - 1) / kHistChunk;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    hipLaunchKernelGGL(topk_long_hist_kernel<TRANSLATE>, dim3(num_rows, nchunk), dim3(kLongNT), 0, stream, scores,
+    hipLaunchKernelGGL(topk_long_hist_kernel<TRANSLATE>, dim3(num_rows, nhist), dim3(kLongNT), 0, stream, scores,
                        ld, row_len, max_len, k, sel, sel_count, ws, tr);
     if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
     hipLaunchKernelGGL(topk_long_emit_kernel<TRANSLATE>, dim3(num_rows, nchunk), dim3(kLongNT), 0, stream, scores,
