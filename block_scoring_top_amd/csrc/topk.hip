@@ -48,6 +48,9 @@ namespace bs {
 constexpr int kRowNT = 1024;                   // lanes per workgroup, one row per workgroup
 constexpr int kRowVpt = 16;                    // register path: values per lane
 constexpr int kRowCand = 2048;                 // boundary candidates held in LDS (row kernel)
+constexpr int kMidNT = 512;                    // row kernel for rows of 16,385-32,768 entries: lanes per workgroup
+constexpr int kMidVpt = 64;                    // ...values per lane in registers
+constexpr int kMidCand = 2048;                 // ...boundary candidates in LDS
 constexpr int kManyNT = 256;                   // row kernel for many rows: lanes per workgroup
 constexpr int kManyVpt = 64;                   // ...values per lane in registers
 constexpr int kManyCand = 1024;                // ...boundary candidates in LDS
@@ -792,21 +795,24 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float
   }
 }
 
-// One workgroup of NT lanes per row.  Two shapes: 1,024 lanes holding 16
-// entries each when the batch has few rows (each row gets a whole CU), 256
-// lanes holding 64 entries each when it has many (several rows per CU, so
-// one row's latency chain overlaps the others').
+// One workgroup of NT lanes per row.  Three shapes: 1,024 lanes holding 16
+// entries each when the batch has few rows (each row gets a whole CU; longer
+// rows are streamed), 512 lanes holding 64 entries each for rows of up to
+// 32,768 entries (two rows per CU, one pass), 256 lanes holding 64 entries
+// each when it has many rows (several rows per CU, so one row's latency chain
+// overlaps the others').
 template <bool TRANSLATE, int NT, int VPT, int CAP>
-__global__ __launch_bounds__(NT, NT == kManyNT ? 4 : 1) void topk_rows_kernel(
+__global__ __launch_bounds__(NT, NT == kManyNT ? 4 : NT == kMidNT ? 2 : 1) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
     int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, Translate tr) {
   __shared__ TopkShared<CAP> s;
   const int r = blockIdx.x;
   const int n = max(0, min(row_len[r], max_len));
   const int m = min(k, n);
-  // The many-rows shape is launched only for rows of at most NT*VPT entries.
-  select_whole_row<NT, VPT, CAP, TRANSLATE, NT != kManyNT>(s, scores + (int64_t)r * ld, n, m, k,
-                                                           sel + (int64_t)r * k, sel_count, r, tr);
+  // The many-rows and mid shapes are launched only for rows of at most
+  // NT*VPT entries.
+  select_whole_row<NT, VPT, CAP, TRANSLATE, NT == kRowNT>(s, scores + (int64_t)r * ld, n, m, k,
+                                                          sel + (int64_t)r * k, sel_count, r, tr);
 }
 
 // Output entries of selection position q (block j of a long-row chunk),
@@ -1065,6 +1071,9 @@ static int launch_select(const float* scores, int64_t ld, const int32_t* row_len
                        ld, row_len, max_len, k, sel, sel_count, ws, tr);
   } else if (num_rows >= kManyMinRows && max_len <= kManyNT * kManyVpt) {
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kManyNT, kManyVpt, kManyCand>), dim3(num_rows), dim3(kManyNT), 0,
+                       stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
+  } else if (max_len > kRowNT * kRowVpt && max_len <= kMidNT * kMidVpt) {
+    hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kMidNT, kMidVpt, kMidCand>), dim3(num_rows), dim3(kMidNT), 0,
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   } else {
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kRowNT, kRowVpt, kRowCand>), dim3(num_rows), dim3(kRowNT), 0,
