@@ -174,8 +174,7 @@ def run_workload(name, K, warmup, dev, fused=True):
         sel = torch.empty((inp.num_rows, inp.k), dtype=torch.int32, device=dev)
         cnt = torch.empty(inp.num_rows, dtype=torch.int32, device=dev)
         ws = bst.topk_workspace(inp.num_rows, inp.max_len, inp.k, dev)
-        ms, t_topk = time_steps([lambda: bst.topk_select_rows(s, rl, inp.max_len, inp.k, sel, cnt, ws)],
-                                K, warmup, stream)
+        ms, t_topk = time_steps([bst.prepare_topk(s, rl, inp.max_len, inp.k, sel, cnt, ws)], K, warmup, stream)
         alg = inp.num_rows * inp.max_len * 4 + inp.num_rows * inp.k * 4
         ach = alg / (t_topk * 1e-3) / 1e9
         log(f"{name}: {ms * 1e3:.1f} us/step (top-k {t_topk * 1e3:.1f} us)")
@@ -189,7 +188,7 @@ def run_workload(name, K, warmup, dev, fused=True):
     scorer = "prefill" if name == "qsa_prefill_8k" else "decode"
     path = IndexerPath(upload(inp, dev), scorer)
     if fused:
-        fns, names = [path.score, path.select_translate], ["score", "select_translate"]
+        fns, names = list(path.prepared()), ["score", "select_translate"]
     else:
         fns, names = [path.score, path.select, path.expand], ["score", "topk", "expand"]
     ms, t_score = time_steps(fns, K, warmup, stream, probe=0)

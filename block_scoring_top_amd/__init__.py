@@ -100,8 +100,8 @@ _I32 = (torch.int32,)
 _F32 = (torch.float32,)
 
 
-def _score(fn: str, q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores,
-           row_len=None, stream=None):
+def _score_args(q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores, row_len=None):
+    """Checked argument tuple of a scorer call (all but the stream)."""
     dev = q.device
     num_rows = int(row_pos.shape[0])
     num_req = int(req_row_ptr.shape[0]) - 1
@@ -114,14 +114,18 @@ def _score(fn: str, q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, m
     per_page = PAGE_TOKENS // int(c) if int(c) in (1, 4) else 1
     if kcache.numel() < int(num_pages) * per_page * DIM:
         raise ValueError("kcache holds fewer than num_pages pages")
-    st = getattr(lib(), fn)(
-        _ptr(q, _BF16, "q", dev), _ptr(kcache, _BF16, "kcache", dev), int(num_pages),
-        _ptr(page_table, _I32, "page_table", dev), int(page_table.shape[1]),
-        _ptr(req_row_ptr, _I32, "req_row_ptr", dev), num_req,
-        _ptr(row_pos, _I32, "row_pos", dev), num_rows, int(c), int(max_vis),
-        _ptr(scores, _F32, "scores", dev), int(scores.stride(0)),
-        _ptr(row_len, _I32, "row_len", dev), _stream(stream, dev))
-    _check(st, fn)
+    return (_ptr(q, _BF16, "q", dev), _ptr(kcache, _BF16, "kcache", dev), int(num_pages),
+            _ptr(page_table, _I32, "page_table", dev), int(page_table.shape[1]),
+            _ptr(req_row_ptr, _I32, "req_row_ptr", dev), num_req,
+            _ptr(row_pos, _I32, "row_pos", dev), num_rows, int(c), int(max_vis),
+            _ptr(scores, _F32, "scores", dev), int(scores.stride(0)),
+            _ptr(row_len, _I32, "row_len", dev))
+
+
+def _score(fn: str, q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores,
+           row_len=None, stream=None):
+    args = _score_args(q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores, row_len)
+    _check(getattr(lib(), fn)(*args, _stream(stream, q.device)), fn)
 
 
 def idx_score_decode(q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores,
@@ -148,8 +152,8 @@ def topk_workspace(num_rows: int, max_len: int, k: int, device) -> Optional[torc
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
-def topk_select_rows(scores, row_len, max_len, k, sel, sel_count, workspace=None, stream=None):
-    """Exact top-k per FP32 row.  See ``topk_select_rows`` in blockscore.h."""
+def _topk_args(scores, row_len, max_len, k, sel, sel_count, workspace=None):
+    """Checked argument tuple of a ``topk_select_rows`` call (all but the stream)."""
     dev = scores.device
     R = int(scores.shape[0])
     if sel.dim() != 2 or sel.shape[0] != R or sel.shape[1] != k:
@@ -157,11 +161,15 @@ def topk_select_rows(scores, row_len, max_len, k, sel, sel_count, workspace=None
     if sel_count.numel() != R or row_len.numel() != R:
         raise ValueError("row_len and sel_count must hold num_rows entries")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().topk_select_rows(
-        _ptr(scores, _F32, "scores", dev), int(scores.stride(0)), _ptr(row_len, _I32, "row_len", dev), R,
-        int(max_len), int(k), _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev),
-        _ptr(workspace, (torch.uint8,), "workspace", dev), ws_bytes, _stream(stream, dev))
-    _check(st, "topk_select_rows")
+    return (_ptr(scores, _F32, "scores", dev), int(scores.stride(0)), _ptr(row_len, _I32, "row_len", dev), R,
+            int(max_len), int(k), _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev),
+            _ptr(workspace, (torch.uint8,), "workspace", dev), ws_bytes)
+
+
+def topk_select_rows(scores, row_len, max_len, k, sel, sel_count, workspace=None, stream=None):
+    """Exact top-k per FP32 row.  See ``topk_select_rows`` in blockscore.h."""
+    args = _topk_args(scores, row_len, max_len, k, sel, sel_count, workspace)
+    _check(lib().topk_select_rows(*args, _stream(stream, scores.device)), "topk_select_rows")
 
 
 def idx_expand_translate(sel, sel_count, k, req_row_ptr, row_pos, c, page_table, out_slots, out_count,
@@ -185,9 +193,9 @@ def idx_expand_translate(sel, sel_count, k, req_row_ptr, row_pos, c, page_table,
     _check(st, "idx_expand_translate")
 
 
-def idx_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
-                         out_slots, out_count, out_pos=None, workspace=None, stream=None):
-    """Top-k and expand/translate in one kernel.  See ``idx_select_translate`` in blockscore.h."""
+def _select_translate_args(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                           out_slots, out_count, out_pos=None, workspace=None):
+    """Checked argument tuple of an ``idx_select_translate`` call (all but the stream)."""
     dev = scores.device
     R = int(scores.shape[0])
     if sel.dim() != 2 or sel.shape[0] != R or sel.shape[1] != k:
@@ -199,19 +207,66 @@ def idx_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, c, p
     if out_pos is not None and out_pos.shape != out_slots.shape:
         raise ValueError("out_pos must match out_slots")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().idx_select_translate(
-        _ptr(scores, _F32, "scores", dev), int(scores.stride(0)), _ptr(row_len, _I32, "row_len", dev), R,
-        int(max_len), int(k), _ptr(req_row_ptr, _I32, "req_row_ptr", dev), int(req_row_ptr.shape[0]) - 1,
-        _ptr(row_pos, _I32, "row_pos", dev), int(c), _ptr(page_table, _I32, "page_table", dev),
-        int(page_table.shape[1]), _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev),
-        _ptr(out_slots, _I32, "out_slots", dev), _ptr(out_pos, _I32, "out_pos", dev),
-        _ptr(out_count, _I32, "out_count", dev), int(out_slots.stride(0)),
-        _ptr(workspace, (torch.uint8,), "workspace", dev), ws_bytes, _stream(stream, dev))
-    _check(st, "idx_select_translate")
+    return (_ptr(scores, _F32, "scores", dev), int(scores.stride(0)), _ptr(row_len, _I32, "row_len", dev), R,
+            int(max_len), int(k), _ptr(req_row_ptr, _I32, "req_row_ptr", dev), int(req_row_ptr.shape[0]) - 1,
+            _ptr(row_pos, _I32, "row_pos", dev), int(c), _ptr(page_table, _I32, "page_table", dev),
+            int(page_table.shape[1]), _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev),
+            _ptr(out_slots, _I32, "out_slots", dev), _ptr(out_pos, _I32, "out_pos", dev),
+            _ptr(out_count, _I32, "out_count", dev), int(out_slots.stride(0)),
+            _ptr(workspace, (torch.uint8,), "workspace", dev), ws_bytes)
+
+
+def idx_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                         out_slots, out_count, out_pos=None, workspace=None, stream=None):
+    """Top-k and expand/translate in one kernel.  See ``idx_select_translate`` in blockscore.h."""
+    args = _select_translate_args(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel,
+                                  sel_count, out_slots, out_count, out_pos, workspace)
+    _check(lib().idx_select_translate(*args, _stream(stream, scores.device)), "idx_select_translate")
+
+
+class PreparedCall:
+    """One C call with its arguments checked and marshalled once (the tensors
+    behind the pointers must outlive it); ``__call__`` adds the stream and
+    checks the status.  For loops that issue the same call many times."""
+
+    def __init__(self, fn: str, args: tuple, device):
+        self.fn = fn
+        self.args = args
+        self.device = device
+        self._f = getattr(lib(), fn)
+
+    def __call__(self, stream=None):
+        st = self._f(*self.args, _stream(stream, self.device))
+        if st != 0:
+            _check(st, self.fn)
+
+
+def prepare_score(fn: str, q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores,
+                  row_len=None) -> PreparedCall:
+    """``idx_score_decode`` or ``idx_score_prefill`` with fixed arguments."""
+    if fn not in ("idx_score_decode", "idx_score_prefill"):
+        raise ValueError("fn must be idx_score_decode or idx_score_prefill")
+    return PreparedCall(fn, _score_args(q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis,
+                                        scores, row_len), q.device)
+
+
+def prepare_topk(scores, row_len, max_len, k, sel, sel_count, workspace=None) -> PreparedCall:
+    """``topk_select_rows`` with fixed arguments."""
+    return PreparedCall("topk_select_rows", _topk_args(scores, row_len, max_len, k, sel, sel_count, workspace),
+                        scores.device)
+
+
+def prepare_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                             out_slots, out_count, out_pos=None, workspace=None) -> PreparedCall:
+    """``idx_select_translate`` with fixed arguments."""
+    return PreparedCall("idx_select_translate",
+                        _select_translate_args(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table,
+                                               sel, sel_count, out_slots, out_count, out_pos, workspace),
+                        scores.device)
 
 
 __all__ = [
     "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
     "topk_select_rows", "idx_expand_translate", "idx_select_translate", "status_string", "BlockScoreError",
-    "lib",
+    "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate",
 ]

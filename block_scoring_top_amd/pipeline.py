@@ -9,7 +9,7 @@ from __future__ import annotations
 import torch
 
 from . import (idx_expand_translate, idx_score_decode, idx_score_prefill, idx_select_translate,
-               topk_select_rows, topk_workspace)
+               prepare_score, prepare_select_translate, topk_select_rows, topk_workspace)
 
 
 class IndexerPath:
@@ -38,6 +38,19 @@ class IndexerPath:
         self.pos = torch.empty((R, ld_out), dtype=torch.int32, device=dev)
         self.out_count = torch.empty(R, dtype=torch.int32, device=dev)
         self.workspace = topk_workspace(R, int(inp.max_vis), inp.k, dev)
+        self._prepared = None
+
+    def _prepare(self):
+        """The two calls of the fused path with their arguments checked and
+        marshalled once (``run`` then costs two plain C calls on the host)."""
+        i = self.inp
+        fn = "idx_score_decode" if self.scorer == "decode" else "idx_score_prefill"
+        self._prepared = (
+            prepare_score(fn, i.q, i.kcache, i.num_pages, i.page_table, i.req_row_ptr, i.row_pos, i.c, i.max_vis,
+                          self.scores, self.row_len),
+            prepare_select_translate(self.scores, self.row_len, int(i.max_vis), i.k, i.req_row_ptr, i.row_pos,
+                                     i.c, i.page_table, self.sel, self.sel_count, self.slots, self.out_count,
+                                     out_pos=self.pos, workspace=self.workspace))
 
     def score(self, stream=None):
         i = self.inp
@@ -61,12 +74,21 @@ class IndexerPath:
                              i.page_table, self.sel, self.sel_count, self.slots, self.out_count, out_pos=self.pos,
                              workspace=self.workspace, stream=stream)
 
+    def prepared(self):
+        """(score, select_translate) as prepared calls: each takes an optional
+        stream and launches with no per-call argument checking."""
+        if self._prepared is None:
+            self._prepare()
+        return self._prepared
+
     def run(self, stream=None, fused: bool = True):
         """One pass of the path: score, then select + translate (fused into one
         kernel, the default) or the separate select and expand calls."""
-        self.score(stream)
         if fused:
-            self.select_translate(stream)
+            score, select_translate = self.prepared()
+            score(stream)
+            select_translate(stream)
         else:
+            self.score(stream)
             self.select(stream)
             self.expand(stream)
