@@ -144,3 +144,20 @@ def test_product_path_does_not_import_the_oracle():
             text = open(path).read()
             assert "import oracle" not in text and "from oracle" not in text, path
             assert "liboracle" not in text, path
+
+
+def test_prepared_calls_check_their_arguments_when_prepared():
+    # Argument checking happens once, when the call is prepared (CPU tensors,
+    # wrong dtypes and wrong shapes are rejected there, before any HIP call).
+    import torch
+    q = torch.zeros((2, 4, 128), dtype=torch.int16)
+    i32 = torch.zeros(3, dtype=torch.int32)
+    f32 = torch.zeros((2, 8), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        bst.prepare_score("idx_score_decode", q, q, 1, i32.view(1, 3), i32[:2], i32[:2], 4, 8, f32)
+    with pytest.raises(ValueError):
+        bst.prepare_score("idx_score_sideways", q, q, 1, i32.view(1, 3), i32[:2], i32[:2], 4, 8, f32)
+    with pytest.raises((TypeError, ValueError)):
+        bst.prepare_topk(f32, i32[:2], 8, 4, torch.zeros((2, 4), dtype=torch.int64), i32[:2])
+    with pytest.raises(ValueError):
+        bst.prepare_topk(f32, i32[:2], 8, 4, torch.zeros((2, 5), dtype=torch.int32), i32[:2])

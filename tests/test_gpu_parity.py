@@ -244,6 +244,34 @@ def test_e2e_dsa_16x80k_full(fused):
     _full_check(synth.dsa_decode_16x80k(), fused=fused)
 
 
+def test_prepared_calls_match_the_public_calls():
+    # The pipeline launches through prepared calls; the public functions check
+    # and marshal on every call.  Both run the same kernels on the same inputs.
+    import torch
+    from block_scoring_top_amd.pipeline import IndexerPath
+    from synth.device import upload
+    inp = synth.qsa_verify_64req(B=5, lo=300, hi=40000)
+    d = upload(inp, "cuda")
+    a = IndexerPath(d, "decode")
+    a.run()
+    b = IndexerPath(d, "decode")
+    b.score()
+    b.select_translate()
+    torch.cuda.synchronize()
+    for x, y in ((a.row_len, b.row_len), (a.sel_count, b.sel_count), (a.out_count, b.out_count)):
+        assert torch.equal(x, y)
+    for r in range(d.num_rows):
+        v = int(a.row_len[r])  # entries past the visible range are left untouched (uninitialised here)
+        assert torch.equal(a.scores[r, :v].isnan(), b.scores[r, :v].isnan())
+        assert torch.equal(a.scores[r, :v].nan_to_num(), b.scores[r, :v].nan_to_num())
+        n = int(a.sel_count[r])
+        assert torch.equal(a.sel[r, :n].sort().values, b.sel[r, :n].sort().values)
+        m = int(a.out_count[r])
+        pa, pb = a.pos[r, :m], b.pos[r, :m]
+        oa, ob = pa.argsort(), pb.argsort()
+        assert torch.equal(pa[oa], pb[ob]) and torch.equal(a.slots[r, :m][oa], b.slots[r, :m][ob])
+
+
 def test_fused_select_translate_on_given_rows():
     # idx_select_translate on given FP32 rows (tie storms, long and short rows
     # in one batch) against the oracle's top-k and expand of the same rows
