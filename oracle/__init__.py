@@ -35,6 +35,8 @@ def lib():
         L.oracle_topk.restype = C.c_int
         L.oracle_expand_translate.argtypes = [P, P, i32, P, i32, P, i32, i32, P, i32, P, P, P, i32]
         L.oracle_expand_translate.restype = C.c_int
+        L.oracle_expand_translate_shared.argtypes = [P, P, i32, P, i32, P, P, i32, i32, i32, P, i32, P, P, P, i32]
+        L.oracle_expand_translate_shared.restype = C.c_int
         L.oracle_f32_to_f16.argtypes = [C.c_uint32]
         L.oracle_f32_to_f16.restype = C.c_uint16
         L.oracle_key16.argtypes = [C.c_uint16]
@@ -126,6 +128,32 @@ def expand_translate(inp, sel: np.ndarray, count: np.ndarray, ld_out: int | None
                                        int(inp.c), _p(pt), pt.shape[1], _p(slots), _p(pos), _p(oc), ld_out)
     if st != 0:
         raise OracleError("oracle_expand_translate failed: %d" % st)
+    return slots, pos, oc
+
+
+def expand_translate_shared(inp, sel: np.ndarray, count: np.ndarray, row_pos_now, max_advance: int,
+                            ld_out: int | None = None):
+    """IndexShare expansion (QSA page, section IndexShare MTP): the selection
+    captured at each row's inp.row_pos is expanded as by expand_translate, and
+    the tail runs from the captured pending tokens through row_pos_now.
+    Returns (slots, positions, count), canonical order, -1 padded."""
+    ld_out = int(inp.ld_out + max_advance if ld_out is None else ld_out)
+    R = inp.num_rows
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    cnt = np.ascontiguousarray(count, dtype=np.int32)
+    now = np.ascontiguousarray(row_pos_now, dtype=np.int32)
+    k = sel.shape[1]
+    slots = np.empty((R, ld_out), dtype=np.int32)
+    pos = np.empty((R, ld_out), dtype=np.int32)
+    oc = np.empty(R, dtype=np.int32)
+    pt = np.ascontiguousarray(inp.page_table, dtype=np.int32)
+    ptr = np.ascontiguousarray(inp.req_row_ptr, dtype=np.int32)
+    rp = np.ascontiguousarray(inp.row_pos, dtype=np.int32)
+    st = lib().oracle_expand_translate_shared(_p(sel), _p(cnt), k, _p(ptr), ptr.shape[0] - 1, _p(rp), _p(now), R,
+                                              int(inp.c), int(max_advance), _p(pt), pt.shape[1], _p(slots),
+                                              _p(pos), _p(oc), ld_out)
+    if st != 0:
+        raise OracleError("oracle_expand_translate_shared failed: %d" % st)
     return slots, pos, oc
 
 

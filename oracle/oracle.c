@@ -24,6 +24,10 @@
  *                            pending; TopK-V2 Figure 2 caption: translation to
  *                            physical KV-cache slots; vllm-sparse-mla-blackwell,
  *                            shadowgraph.io, Design notes: index >= 0 sentinel).
+ *   oracle_expand_translate_shared  the same with the tail extended to the
+ *                            row's current position (QSA section, IndexShare
+ *                            MTP: a captured selection reused across draft
+ *                            steps, the positions drafted since appended).
  *   oracle_topk_hist         the TopK-V2 steps in the blog's order (FP16 key,
  *                            10-bit bins, threshold bin, direct emission,
  *                            exact refinement of the boundary bin), written
@@ -198,14 +202,13 @@ int oracle_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t
 /* physical slot page_table[p / 64] * 64 + p mod 64.  Canonical order: block  */
 /* positions ascending, then pending positions ascending; -1 pads the row.    */
 /* ------------------------------------------------------------------------ */
-int oracle_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_t k,
-                            const int32_t* req_row_ptr, int32_t num_req,
-                            const int32_t* row_pos, int32_t num_rows, int32_t c,
-                            const int32_t* page_table, int32_t pt_stride,
-                            int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
-                            int32_t ld_out) {
-  if (c != 1 && c != 4) return OR_ERR_ARG;
-  if (k < 1 || num_rows < 0 || num_req < 0 || ld_out < k * c + c - 1) return OR_ERR_ARG;
+/* Rows of one expansion; the pending tail of row r ends at tail_end[r]      */
+/* (its own position when tail_end is NULL).                                 */
+static int expand_rows(const int32_t* sel, const int32_t* sel_count, int32_t k,
+                       const int32_t* req_row_ptr, int32_t num_req, const int32_t* row_pos,
+                       const int32_t* tail_end, int32_t max_advance, int32_t c,
+                       const int32_t* page_table, int32_t pt_stride,
+                       int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out) {
   int status = OR_OK;
   for (int32_t b = 0; b < num_req; ++b) {
     for (int32_t r = req_row_ptr[b]; r < req_row_ptr[b + 1]; ++r) {
@@ -214,9 +217,13 @@ int oracle_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_
       for (int32_t i = 0; i < ld_out; ++i) slots[i] = pos[i] = -1;
       out_count[r] = 0;
       const int32_t t = row_pos[r];
+      const int32_t te = tail_end ? tail_end[r] : t;
       const int32_t nv = oracle_n_vis(t, c);
       const int32_t m = sel_count[r];
-      if (t < 0 || m < 0 || m > k || ((int64_t)t / OR_PAGE) >= pt_stride) { status = OR_ERR_DATA; continue; }
+      if (t < 0 || m < 0 || m > k || te < t || te - t > max_advance || ((int64_t)te / OR_PAGE) >= pt_stride) {
+        status = OR_ERR_DATA;
+        continue;
+      }
       int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)(m > 0 ? m : 1));
       memcpy(blocks, sel + (int64_t)r * k, sizeof(int32_t) * (size_t)m);
       qsort(blocks, (size_t)m, sizeof(int32_t), int_asc);
@@ -227,7 +234,7 @@ int oracle_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_
       int32_t n = 0;
       for (int32_t i = 0; i < m; ++i)
         for (int32_t u = 0; u < c; ++u) pos[n++] = c * blocks[i] + u;
-      for (int32_t p = c * nv; p <= t; ++p) pos[n++] = p;
+      for (int32_t p = c * nv; p <= te; ++p) pos[n++] = p;
       for (int32_t i = 0; i < n; ++i) {
         const int32_t page = page_table[(int64_t)b * pt_stride + pos[i] / OR_PAGE];
         slots[i] = page < 0 ? -1 : page * OR_PAGE + pos[i] % OR_PAGE;
@@ -239,6 +246,41 @@ int oracle_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_
     }
   }
   return status;
+}
+
+int oracle_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_t k,
+                            const int32_t* req_row_ptr, int32_t num_req,
+                            const int32_t* row_pos, int32_t num_rows, int32_t c,
+                            const int32_t* page_table, int32_t pt_stride,
+                            int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
+                            int32_t ld_out) {
+  if (c != 1 && c != 4) return OR_ERR_ARG;
+  if (k < 1 || num_rows < 0 || num_req < 0 || ld_out < k * c + c - 1) return OR_ERR_ARG;
+  return expand_rows(sel, sel_count, k, req_row_ptr, num_req, row_pos, NULL, 0, c, page_table, pt_stride,
+                     out_slots, out_pos, out_count, ld_out);
+}
+
+/* ------------------------------------------------------------------------ */
+/* IndexShare expansion (QSA page, section "IndexShare MTP"): a selection    */
+/* captured for a row at position t0 is kept while the row advances; at      */
+/* position t1 (t0 <= t1 <= t0 + max_advance) the chosen blocks expand as    */
+/* before and the tail holds the captured pending tokens followed by every   */
+/* position since, i.e. c*n_vis(t0) .. t1.  ld_out >= k*c + c - 1 +          */
+/* max_advance.                                                              */
+/* ------------------------------------------------------------------------ */
+int oracle_expand_translate_shared(const int32_t* sel, const int32_t* sel_count, int32_t k,
+                                   const int32_t* req_row_ptr, int32_t num_req,
+                                   const int32_t* row_pos, const int32_t* row_pos_now, int32_t num_rows,
+                                   int32_t c, int32_t max_advance,
+                                   const int32_t* page_table, int32_t pt_stride,
+                                   int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
+                                   int32_t ld_out) {
+  if (c != 1 && c != 4) return OR_ERR_ARG;
+  if (k < 1 || num_rows < 0 || num_req < 0 || max_advance < 0 || max_advance > 1024 ||
+      ld_out < k * c + c - 1 + max_advance)
+    return OR_ERR_ARG;
+  return expand_rows(sel, sel_count, k, req_row_ptr, num_req, row_pos, row_pos_now, max_advance, c, page_table,
+                     pt_stride, out_slots, out_pos, out_count, ld_out);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -445,3 +445,89 @@ def test_pipeline_config_shapes():
     assert out["row_len"].tolist() == [2048]
     assert out["sel_count"].tolist() == [512]
     assert out["out_count"].tolist() == [2050]
+
+
+# ---------------------------------------------------------------------------
+# IndexShare expansion (QSA page, section IndexShare MTP): a selection
+# captured at t0 is reused while the row advances to t1; the tail holds the
+# captured pending tokens and every position since.
+# ---------------------------------------------------------------------------
+
+def _shared_batch(rng, c, k, rows_per_req, advance_room):
+    # contexts long enough that every position up to t0 + advance_room has a page
+    ctx, row_pos = [], []
+    for rows in rows_per_req:
+        ctx.append(max(rows) + advance_room + 1)
+        row_pos.append(rows)
+    return synth.build_paged_batch("shared", 5, c=c, k=k, ctx_tokens=ctx, row_pos_per_req=row_pos, rng=rng)
+
+
+def test_shared_expand_worked_example():
+    # c = 4, captured at t0 = 10: blocks 0 and 1 are visible (tokens 0..7),
+    # tokens 8, 9, 10 are pending.  Chosen block: 1 (tokens 4..7).  At t1 = 13
+    # the tail is 8..13, so the positions are 4 5 6 7 8 9 10 11 12 13.
+    rng = np.random.default_rng(41)
+    inp = synth.build_paged_batch("ex", 6, c=4, k=4, ctx_tokens=[64], row_pos_per_req=[[10]], rng=rng,
+                                  identity_pages=True)
+    sel = np.array([[1, -1, -1, -1]], dtype=np.int32)
+    slots, pos, oc = oracle.expand_translate_shared(inp, sel, np.array([1], dtype=np.int32), [13], 3)
+    assert oc[0] == 10
+    assert pos[0, :10].tolist() == [4, 5, 6, 7, 8, 9, 10, 11, 12, 13]
+    assert slots[0, :10].tolist() == pos[0, :10].tolist()  # identity pages
+    assert np.all(pos[0, 10:] == -1) and np.all(slots[0, 10:] == -1)
+
+
+def test_shared_expand_without_advance_is_the_plain_expansion():
+    rng = np.random.default_rng(42)
+    for c in (1, 4):
+        inp = _shared_batch(rng, c, 64, [[300, 301, 302], [517], [1000, 1003]], advance_room=8)
+        out = oracle.pipeline(inp)
+        for adv_room in (0, 5):
+            s2, p2, o2 = oracle.expand_translate_shared(inp, out["sel"], out["sel_count"], inp.row_pos, adv_room)
+            assert np.array_equal(o2, out["out_count"])
+            w = inp.ld_out
+            assert np.array_equal(p2[:, :w], out["pos"]) and np.array_equal(s2[:, :w], out["slots"])
+            assert np.all(p2[:, w:] == -1) and np.all(s2[:, w:] == -1)
+
+
+def test_shared_expand_invariants_and_inverse_translation():
+    rng = np.random.default_rng(43)
+    N = 6
+    for c in (1, 4):
+        rows = [[int(x)] for x in rng.integers(8, 5000, 12)]
+        inp = _shared_batch(rng, c, 128, rows, advance_room=N)
+        out = oracle.pipeline(inp)
+        adv = rng.integers(0, N + 1, inp.num_rows)
+        now = inp.row_pos + adv.astype(np.int32)
+        slots, pos, oc = oracle.expand_translate_shared(inp, out["sel"], out["sel_count"], now, N)
+        inv = {}
+        for b in range(inp.num_req):
+            for lp, pp in enumerate(inp.page_table[b]):
+                if pp >= 0:
+                    inv[int(pp)] = (b, lp)
+        for b in range(inp.num_req):
+            for r in range(inp.req_row_ptr[b], inp.req_row_ptr[b + 1]):
+                t0, t1 = int(inp.row_pos[r]), int(now[r])
+                nv = (t0 + 1) // c
+                m = int(out["sel_count"][r])
+                n = int(oc[r])
+                assert n == c * m + (t1 - c * nv + 1) <= inp.ld_out + N
+                pr = pos[r, :n]
+                assert np.unique(pr).size == n and pr.min() >= 0 and pr.max() <= t1
+                assert pr[c * m:].tolist() == list(range(c * nv, t1 + 1))
+                assert pr[:c * m].tolist() == out["pos"][r, :c * m].tolist()
+                for s_, q_ in zip(slots[r, :n], pr):
+                    bb, lp = inv[int(s_) // 64]
+                    assert bb == b and lp * 64 + int(s_) % 64 == q_
+                assert np.all(slots[r, n:] == -1) and np.all(pos[r, n:] == -1)
+
+
+def test_shared_expand_rejects_bad_advances():
+    rng = np.random.default_rng(44)
+    inp = _shared_batch(rng, 4, 16, [[200]], advance_room=4)
+    out = oracle.pipeline(inp)
+    for now, room in (([199], 4), ([205], 4), ([203], 2)):  # behind t0; beyond t0 + room
+        with pytest.raises(oracle.OracleError):
+            oracle.expand_translate_shared(inp, out["sel"], out["sel_count"], now, room)
+    with pytest.raises(oracle.OracleError):  # ld_out below k*c + c - 1 + max_advance
+        oracle.expand_translate_shared(inp, out["sel"], out["sel_count"], [201], 4, ld_out=inp.ld_out + 3)
