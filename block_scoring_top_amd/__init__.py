@@ -9,6 +9,8 @@ module raises on first use.
 
 Steps (same names as the C ABI):
   idx_score_decode / idx_score_prefill  ->  topk_select_rows  ->  idx_expand_translate
+  (idx_select_translate: the last two in one kernel; idx_expand_translate_shared:
+  the expansion of a selection reused across speculative draft steps)
 """
 from __future__ import annotations
 
@@ -54,6 +56,8 @@ def lib():
         L.topk_select_rows.restype = C.c_int
         L.idx_expand_translate.argtypes = [P, P, i32, P, i32, P, i32, i32, P, i32, P, P, P, i32, P]
         L.idx_expand_translate.restype = C.c_int
+        L.idx_expand_translate_shared.argtypes = [P, P, i32, P, i32, P, P, i32, i32, i32, P, i32, P, P, P, i32, P]
+        L.idx_expand_translate_shared.restype = C.c_int
         L.idx_select_translate.argtypes = [P, i64, P, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P, P, i32,
                                            P, C.c_size_t, P]
         L.idx_select_translate.restype = C.c_int
@@ -193,6 +197,30 @@ def idx_expand_translate(sel, sel_count, k, req_row_ptr, row_pos, c, page_table,
     _check(st, "idx_expand_translate")
 
 
+def idx_expand_translate_shared(sel, sel_count, k, req_row_ptr, row_pos, row_pos_now, c, max_advance, page_table,
+                                out_slots, out_count, out_pos=None, stream=None):
+    """Expansion of a selection reused across draft steps (IndexShare).  See
+    ``idx_expand_translate_shared`` in blockscore.h."""
+    dev = sel.device
+    R = int(row_pos.shape[0])
+    if sel.dim() != 2 or sel.shape[0] != R or sel.shape[1] != k:
+        raise ValueError("sel must be [num_rows, k]")
+    if row_pos_now.numel() != R or sel_count.numel() != R:
+        raise ValueError("row_pos_now and sel_count must hold num_rows entries")
+    if out_slots.dim() != 2 or out_slots.shape[0] != R:
+        raise ValueError("out_slots must be [num_rows, ld_out]")
+    if out_pos is not None and out_pos.shape != out_slots.shape:
+        raise ValueError("out_pos must match out_slots")
+    st = lib().idx_expand_translate_shared(
+        _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev), int(k),
+        _ptr(req_row_ptr, _I32, "req_row_ptr", dev), int(req_row_ptr.shape[0]) - 1,
+        _ptr(row_pos, _I32, "row_pos", dev), _ptr(row_pos_now, _I32, "row_pos_now", dev), R, int(c),
+        int(max_advance), _ptr(page_table, _I32, "page_table", dev), int(page_table.shape[1]),
+        _ptr(out_slots, _I32, "out_slots", dev), _ptr(out_pos, _I32, "out_pos", dev),
+        _ptr(out_count, _I32, "out_count", dev), int(out_slots.stride(0)), _stream(stream, dev))
+    _check(st, "idx_expand_translate_shared")
+
+
 def _select_translate_args(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
                            out_slots, out_count, out_pos=None, workspace=None):
     """Checked argument tuple of an ``idx_select_translate`` call (all but the stream)."""
@@ -267,6 +295,7 @@ def prepare_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, 
 
 __all__ = [
     "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
-    "topk_select_rows", "idx_expand_translate", "idx_select_translate", "status_string", "BlockScoreError",
+    "topk_select_rows", "idx_expand_translate", "idx_expand_translate_shared", "idx_select_translate",
+    "status_string", "BlockScoreError",
     "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate",
 ]

@@ -88,8 +88,29 @@ BS_EXPORT int idx_expand_translate(const int32_t* sel, const int32_t* sel_count,
   if (!sel || !sel_count || !req_row_ptr || !row_pos || !page_table || !out_slots || !out_count)
     return BS_ERR_NULL;
   if (pt_stride < 1) return BS_ERR_ARG;
-  return bs::launch_expand(sel, sel_count, k, req_row_ptr, num_req, row_pos, num_rows, c, page_table, pt_stride,
-                           out_slots, out_pos, out_count, ld_out, static_cast<hipStream_t>(stream));
+  return bs::launch_expand(sel, sel_count, k, req_row_ptr, num_req, row_pos, nullptr, 0, num_rows, c, page_table,
+                           pt_stride, out_slots, out_pos, out_count, ld_out, static_cast<hipStream_t>(stream));
+}
+
+BS_EXPORT int idx_expand_translate_shared(const int32_t* sel, const int32_t* sel_count, int32_t k,
+                                          const int32_t* req_row_ptr, int32_t num_req,
+                                          const int32_t* row_pos, const int32_t* row_pos_now, int32_t num_rows,
+                                          int32_t c, int32_t max_advance,
+                                          const int32_t* page_table, int32_t pt_stride,
+                                          int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
+                                          int32_t ld_out, void* stream) {
+  if (num_rows < 0 || num_req < 0 || k < 1 || k > BS_KMAX) return BS_ERR_ARG;
+  if (c != 1 && c != 4) return BS_ERR_ARG;
+  if (max_advance < 0 || max_advance > BS_MAX_ADVANCE) return BS_ERR_ARG;
+  if ((int64_t)ld_out < (int64_t)k * c + c - 1 + max_advance) return BS_ERR_ARG;
+  if (num_rows == 0) return BS_OK;
+  if (num_req == 0) return BS_ERR_ARG;  // rows need a request
+  if (!sel || !sel_count || !req_row_ptr || !row_pos || !row_pos_now || !page_table || !out_slots || !out_count)
+    return BS_ERR_NULL;
+  if (pt_stride < 1) return BS_ERR_ARG;
+  return bs::launch_expand(sel, sel_count, k, req_row_ptr, num_req, row_pos, row_pos_now, max_advance, num_rows, c,
+                           page_table, pt_stride, out_slots, out_pos, out_count, ld_out,
+                           static_cast<hipStream_t>(stream));
 }
 
 BS_EXPORT int idx_select_translate(const float* scores, int64_t ld_scores, const int32_t* row_len,

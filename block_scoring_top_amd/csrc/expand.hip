@@ -8,6 +8,12 @@
 // then translated to physical KV-cache slots.  vllm-sparse-mla-blackwell,
 // Design notes: -1 is the padding sentinel.
 //
+// IndexShare (same QSA page, section IndexShare MTP): a selection captured
+// for a row at position t0 is reused while the row advances; at position t1
+// the tail holds the captured pending tokens and every position drafted
+// since, c*n_vis(t0) .. t1 (row_pos_now != nullptr; t1 is clamped to
+// [t0, t0 + max_advance]).
+//
 // One lane per output entry (a row spans ld_out / 256 workgroups), so every
 // lane does one short chain of dependent loads (selection -> page table) and
 // one coalesced store.
@@ -19,6 +25,7 @@ namespace bs {
 __global__ __launch_bounds__(256) void expand_kernel(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int32_t k,
     const int32_t* __restrict__ req_row_ptr, int32_t num_req, const int32_t* __restrict__ row_pos,
+    const int32_t* __restrict__ row_pos_now, int32_t max_advance,
     int32_t c, const int32_t* __restrict__ page_table, int32_t pt_stride,
     int32_t* __restrict__ out_slots, int32_t* __restrict__ out_pos, int32_t* __restrict__ out_count,
     int32_t ld_out) {
@@ -35,7 +42,8 @@ __global__ __launch_bounds__(256) void expand_kernel(
   b = max(0, min(b, num_req - 1));
   const int t = row_pos[r];
   const int nv = t >= 0 ? (t + 1) / c : 0;
-  const int p = t >= 0 ? t + 1 - c * nv : 0;
+  const int te = (row_pos_now != nullptr && t >= 0) ? min(max(row_pos_now[r], t), t + max_advance) : t;
+  const int p = t >= 0 ? te + 1 - c * nv : 0;  // the tail c*nv .. te
   const int m = max(0, min(sel_count[r], k));
   const int nblk = c * m;
   const int total = nblk + p;
@@ -59,12 +67,13 @@ __global__ __launch_bounds__(256) void expand_kernel(
 }
 
 int launch_expand(const int32_t* sel, const int32_t* sel_count, int32_t k, const int32_t* req_row_ptr,
-                  int32_t num_req, const int32_t* row_pos, int32_t num_rows, int32_t c,
-                  const int32_t* page_table, int32_t pt_stride, int32_t* out_slots, int32_t* out_pos,
-                  int32_t* out_count, int32_t ld_out, hipStream_t stream) {
+                  int32_t num_req, const int32_t* row_pos, const int32_t* row_pos_now, int32_t max_advance,
+                  int32_t num_rows, int32_t c, const int32_t* page_table, int32_t pt_stride, int32_t* out_slots,
+                  int32_t* out_pos, int32_t* out_count, int32_t ld_out, hipStream_t stream) {
   const int chunks = (ld_out + 255) / 256;
   hipLaunchKernelGGL(expand_kernel, dim3(num_rows, chunks), dim3(256), 0, stream, sel, sel_count, k, req_row_ptr,
-                     num_req, row_pos, c, page_table, pt_stride, out_slots, out_pos, out_count, ld_out);
+                     num_req, row_pos, row_pos_now, max_advance, c, page_table, pt_stride, out_slots, out_pos,
+                     out_count, ld_out);
   return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
 }
 

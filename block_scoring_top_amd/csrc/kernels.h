@@ -33,9 +33,12 @@ int launch_select_translate(const float* scores, int64_t ld, const int32_t* row_
                             int32_t* sel, int32_t* sel_count, int32_t* out_slots, int32_t* out_pos,
                             int32_t* out_count, int32_t ld_out, void* workspace, hipStream_t stream);
 
+// row_pos_now == nullptr: the plain expansion; otherwise the IndexShare one
+// (tail through row_pos_now[r], at most max_advance past row_pos[r]).
 int launch_expand(const int32_t* sel, const int32_t* sel_count, int32_t k,
                   const int32_t* req_row_ptr, int32_t num_req,
-                  const int32_t* row_pos, int32_t num_rows, int32_t c,
+                  const int32_t* row_pos, const int32_t* row_pos_now, int32_t max_advance,
+                  int32_t num_rows, int32_t c,
                   const int32_t* page_table, int32_t pt_stride,
                   int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
                   int32_t ld_out, hipStream_t stream);

@@ -5,6 +5,9 @@
  *   1. score   - idx_score_decode / idx_score_prefill
  *   2. select  - topk_select_rows
  *   3. expand  - idx_expand_translate
+ * plus idx_select_translate (steps 2 and 3 in one kernel) and
+ * idx_expand_translate_shared (step 3 for a selection reused across
+ * speculative draft steps).
  *
  * Sources (pages on the subject):
  *   [QSA]   "Qwen3.8-Flash-Next Day-0 in SGLang" (theainews.cc), section on Qwen
@@ -83,6 +86,7 @@ enum bs_status {
 #define BS_DIM 128        /* head dimension [QSA] */
 #define BS_PAGE_TOKENS 64 /* tokens per KV page */
 #define BS_KMAX 2048      /* largest runtime k [TOPK] */
+#define BS_MAX_ADVANCE 1024 /* largest max_advance of idx_expand_translate_shared */
 
 /*
  * idx_score_decode - paged block scores for decode / speculative-verify rows
@@ -157,7 +161,7 @@ size_t topk_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k);
  * histogram; the bin holding the m-th largest is located, entries in higher
  * bins are emitted directly, and the boundary bin is resolved exactly on the
  * (FP32 key, index) pair by radix selection.  In a large batch each row is
- * done by one workgroup (in registers up to 16,384 entries, else streamed);
+ * done by one workgroup (in registers up to 32,768 entries, else streamed);
  * in a small batch (<= 256 rows) rows of >= 32,769 entries are split over
  * several workgroups whose histograms merge through device-scope atomics.
  * Device preconditions: row_len[r] >= 0 (negative counts as 0); no NaN
@@ -193,6 +197,36 @@ int idx_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_t k
                          const int32_t* page_table, int32_t pt_stride,
                          int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
                          int32_t ld_out, void* stream);
+
+/*
+ * idx_expand_translate_shared - the expansion of a selection reused across
+ * speculative draft steps [QSA, section IndexShare MTP: the selection made
+ * for a request's last accepted row at draft-extend is kept for the whole
+ * draft loop, and at each lookup the positions drafted since are appended so
+ * that the draft still sees its own in-progress tokens].
+ *
+ * For row r of request b the selection sel/sel_count was made at position
+ * t0 = row_pos[r]; the row is now at t1 = row_pos_now[r], t0 <= t1 <= t0 +
+ * max_advance.  Output as idx_expand_translate for t0, except that the tail
+ * runs through t1: chosen blocks become c*j .. c*j+c-1, then positions
+ * c*n_vis(t0) .. t1 follow; out_count[r] = c*m + t1 + 1 - c*n_vis(t0).  With
+ * t1 = t0 the output equals idx_expand_translate's.  out_pos may be NULL.
+ * Positions whose page entry is negative or past pt_stride yield -1.
+ *   max_advance  0 .. BS_MAX_ADVANCE (draft steps + 1, say).
+ *   ld_out       >= k*c + c - 1 + max_advance.
+ * Device precondition: t0 <= t1 <= t0 + max_advance (t1 is clamped into that
+ * range otherwise).
+ * Returns BS_OK, BS_ERR_NULL, BS_ERR_ARG (k outside 1..2048, c not 1 or 4,
+ * max_advance out of range, ld_out too small, negative counts, pt_stride < 1,
+ * num_req == 0 while num_rows > 0) or BS_ERR_LAUNCH.
+ */
+int idx_expand_translate_shared(const int32_t* sel, const int32_t* sel_count, int32_t k,
+                                const int32_t* req_row_ptr, int32_t num_req,
+                                const int32_t* row_pos, const int32_t* row_pos_now, int32_t num_rows,
+                                int32_t c, int32_t max_advance,
+                                const int32_t* page_table, int32_t pt_stride,
+                                int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
+                                int32_t ld_out, void* stream);
 
 /*
  * idx_select_translate - topk_select_rows and idx_expand_translate in one

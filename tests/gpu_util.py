@@ -64,6 +64,23 @@ def gpu_expand(inp, sel: np.ndarray, count: np.ndarray):
     return slots.cpu().numpy(), pos.cpu().numpy(), oc.cpu().numpy()
 
 
+def gpu_expand_shared(inp, sel: np.ndarray, count: np.ndarray, row_pos_now: np.ndarray, max_advance: int):
+    say(f"expand shared rows={inp.num_rows} k={inp.k} c={inp.c} max_advance={max_advance}")
+    dev = upload(inp, "cuda")
+    R = inp.num_rows
+    ld_out = inp.ld_out + max_advance
+    s = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
+    c = torch.from_numpy(np.ascontiguousarray(count, dtype=np.int32)).cuda()
+    now = torch.from_numpy(np.ascontiguousarray(row_pos_now, dtype=np.int32)).cuda()
+    slots = torch.full((R, ld_out), -7, dtype=torch.int32, device="cuda")
+    pos = torch.full((R, ld_out), -7, dtype=torch.int32, device="cuda")
+    oc = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    bst.idx_expand_translate_shared(s, c, inp.k, dev.req_row_ptr, dev.row_pos, now, inp.c, max_advance,
+                                    dev.page_table, slots, oc, out_pos=pos)
+    torch.cuda.synchronize()
+    return slots.cpu().numpy(), pos.cpu().numpy(), oc.cpu().numpy()
+
+
 def gpu_scores(inp, scorer: str = "decode", ld: int | None = None):
     say(f"score {scorer}: rows={inp.num_rows} max_vis={inp.max_vis} c={inp.c}")
     dev = upload(inp, "cuda")

@@ -161,3 +161,26 @@ def test_prepared_calls_check_their_arguments_when_prepared():
         bst.prepare_topk(f32, i32[:2], 8, 4, torch.zeros((2, 4), dtype=torch.int64), i32[:2])
     with pytest.raises(ValueError):
         bst.prepare_topk(f32, i32[:2], 8, 4, torch.zeros((2, 5), dtype=torch.int32), i32[:2])
+
+
+def _expand_shared(**kw):
+    a = dict(sel=FAKE, cnt=FAKE, k=512, ptr=FAKE, num_req=1, pos=FAKE, now=FAKE, num_rows=1, c=4, adv=4,
+             pt=FAKE, pt_stride=1, slots=FAKE, opos=NULL, ocnt=FAKE, ld_out=2055, stream=NULL)
+    a.update(kw)
+    return bst.lib().idx_expand_translate_shared(a["sel"], a["cnt"], a["k"], a["ptr"], a["num_req"], a["pos"],
+                                                 a["now"], a["num_rows"], a["c"], a["adv"], a["pt"],
+                                                 a["pt_stride"], a["slots"], a["opos"], a["ocnt"], a["ld_out"],
+                                                 a["stream"])
+
+
+def test_expand_shared_validation():
+    assert _expand_shared(num_rows=0) == BS_OK
+    assert _expand_shared(ld_out=2054) == BS_ERR_ARG       # needs k*c + c - 1 + max_advance = 2055
+    assert _expand_shared(adv=-1) == BS_ERR_ARG
+    assert _expand_shared(adv=1025, ld_out=10000) == BS_ERR_ARG
+    assert _expand_shared(k=0) == BS_ERR_ARG
+    assert _expand_shared(c=2) == BS_ERR_ARG
+    assert _expand_shared(num_req=0) == BS_ERR_ARG
+    assert _expand_shared(pt_stride=0) == BS_ERR_ARG
+    for k in ("sel", "cnt", "ptr", "pos", "now", "pt", "slots", "ocnt"):
+        assert _expand_shared(**{k: NULL}) == BS_ERR_NULL, k

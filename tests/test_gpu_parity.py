@@ -231,6 +231,50 @@ def test_expand_invalid_entries_become_sentinels():
     assert np.all(slots[0, 18:] == -1)
 
 
+def _advancing_batch(rng, c, k, n_req, max_advance):
+    # rows whose contexts hold max_advance more tokens past the rows' positions
+    rows = [[int(x) for x in np.sort(rng.choice(np.arange(8, 20000), int(rng.integers(1, 4)), replace=False))]
+            for _ in range(n_req)]
+    ctx = [max(r) + max_advance + 1 for r in rows]
+    return synth.build_paged_batch("adv", 9, c=c, k=k, ctx_tokens=ctx, row_pos_per_req=rows, rng=rng)
+
+
+@pytest.mark.parametrize("c", [1, 4])
+def test_expand_shared_exact_on_oracle_selection(c):
+    # IndexShare: a selection captured at row_pos, expanded at row_pos + advance
+    rng = np.random.default_rng(60 + c)
+    N = 7
+    inp = _advancing_batch(rng, c, 512 if c == 4 else 2048, 9, N)
+    ref = oracle.pipeline(inp)
+    sel = ref["sel"].copy()
+    for r in range(sel.shape[0]):
+        m = ref["sel_count"][r]
+        sel[r, :m] = rng.permutation(sel[r, :m])
+    adv = rng.integers(0, N + 1, inp.num_rows).astype(np.int32)
+    adv[0], adv[-1] = 0, N
+    now = inp.row_pos + adv
+    rs, rp, rc = oracle.expand_translate_shared(inp, ref["sel"], ref["sel_count"], now, N)
+    slots, pos, oc = gu.gpu_expand_shared(inp, sel, ref["sel_count"], now, N)
+    tail = now + 1 - c * ((inp.row_pos + 1) // c)
+    check_expand_exact(slots, pos, oc, rs, rp, rc, tail)
+
+
+def test_expand_shared_clamps_the_advance():
+    # a current position behind the captured one, or too far ahead, is clamped
+    rng = np.random.default_rng(70)
+    N = 3
+    inp = _advancing_batch(rng, 4, 64, 4, N)
+    ref = oracle.pipeline(inp)
+    now = inp.row_pos.copy()
+    now[0] -= 5           # behind: treated as the captured position
+    now[1:] += N + 9      # too far: treated as the captured position + N
+    clamped = np.clip(now, inp.row_pos, inp.row_pos + N)
+    rs, rp, rc = oracle.expand_translate_shared(inp, ref["sel"], ref["sel_count"], clamped, N)
+    slots, pos, oc = gu.gpu_expand_shared(inp, ref["sel"], ref["sel_count"], now, N)
+    tail = clamped + 1 - 4 * ((inp.row_pos + 1) // 4)
+    check_expand_exact(slots, pos, oc, rs, rp, rc, tail)
+
+
 # ---------------------------------------------------------------------------
 # End to end at the full workload sizes
 # ---------------------------------------------------------------------------
