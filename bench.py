@@ -185,6 +185,8 @@ def run_workload(name, K, warmup, dev, fused=True):
                 "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "topk (all launches)",
                              "algorithmic_bytes": alg, "avg_us": round(t_topk * 1e3, 2)}}
+    if name == "qsa_indexshare_64req":
+        return run_indexshare(name, inp, K, warmup, dev, stream)
     scorer = "prefill" if name == "qsa_prefill_8k" else "decode"
     path = IndexerPath(upload(inp, dev), scorer)
     if fused:
@@ -218,6 +220,46 @@ def run_workload(name, K, warmup, dev, fused=True):
             "kernels_us": {**{n: round(t * 1e3, 2) for n, t in zip(names, br)},
                            "note": "separate pass after the timed region, every call bracketed by HIP events"},
             "roofline": roof}
+
+
+def run_indexshare(name, inp, K, warmup, dev, stream):
+    """A draft step under IndexShare: the selection made at each row's captured
+    position (score + select on the GPU, once, outside the timed region) is
+    expanded at the last draft position, captured + max_advance.  The step is
+    the one idx_expand_translate_shared call."""
+    import torch
+
+    import block_scoring_top_amd as bst
+    import synth
+    from block_scoring_top_amd.pipeline import IndexerPath
+    from synth.device import upload
+
+    d = upload(inp, dev)
+    path = IndexerPath(d, "decode")
+    path.run()
+    adv = synth.INDEXSHARE_MAX_ADVANCE
+    now = (d.row_pos + adv).contiguous()
+    R = d.num_rows
+    ld_out = d.ld_out + adv
+    slots = torch.empty((R, ld_out), dtype=torch.int32, device=dev)
+    pos = torch.empty((R, ld_out), dtype=torch.int32, device=dev)
+    cnt = torch.empty(R, dtype=torch.int32, device=dev)
+    call = bst.prepare_expand_shared(path.sel, path.sel_count, d.k, d.req_row_ptr, d.row_pos, now, d.c, adv,
+                                     d.page_table, slots, cnt, out_pos=pos)
+    ms, t_call = time_steps([call], K, warmup, stream)
+    torch.cuda.synchronize()
+    n_out = int(cnt.sum().item())
+    alg = int(path.sel_count.sum().item()) * 4 + n_out * (4 + 4) + R * 16  # selection in, slots + positions out
+    ach = alg / (t_call * 1e-3) / 1e9
+    log(f"{name}: {ms * 1e3:.1f} us/step (expand of the captured selection at +{adv} positions)")
+    return {"_inp": inp, "rows_per_s": round(R / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+            "config": {"workload": name, "rows": R, "requests": inp.num_req, "k": inp.k, "c": inp.c,
+                       "max_advance": adv, "page_tokens": 64,
+                       "steps": "expand/translate of a captured selection (the draft step's whole indexer work)"},
+            "kernels_us": {"expand_shared": round(t_call * 1e3, 2)},
+            "roofline": {"bound": "latency", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "expand_kernel",
+                         "algorithmic_bytes": alg, "avg_us": round(t_call * 1e3, 2)}}
 
 
 def main():

@@ -197,10 +197,9 @@ def idx_expand_translate(sel, sel_count, k, req_row_ptr, row_pos, c, page_table,
     _check(st, "idx_expand_translate")
 
 
-def idx_expand_translate_shared(sel, sel_count, k, req_row_ptr, row_pos, row_pos_now, c, max_advance, page_table,
-                                out_slots, out_count, out_pos=None, stream=None):
-    """Expansion of a selection reused across draft steps (IndexShare).  See
-    ``idx_expand_translate_shared`` in blockscore.h."""
+def _expand_shared_args(sel, sel_count, k, req_row_ptr, row_pos, row_pos_now, c, max_advance, page_table,
+                        out_slots, out_count, out_pos=None):
+    """Checked argument tuple of an ``idx_expand_translate_shared`` call (all but the stream)."""
     dev = sel.device
     R = int(row_pos.shape[0])
     if sel.dim() != 2 or sel.shape[0] != R or sel.shape[1] != k:
@@ -211,14 +210,21 @@ def idx_expand_translate_shared(sel, sel_count, k, req_row_ptr, row_pos, row_pos
         raise ValueError("out_slots must be [num_rows, ld_out]")
     if out_pos is not None and out_pos.shape != out_slots.shape:
         raise ValueError("out_pos must match out_slots")
-    st = lib().idx_expand_translate_shared(
-        _ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev), int(k),
-        _ptr(req_row_ptr, _I32, "req_row_ptr", dev), int(req_row_ptr.shape[0]) - 1,
-        _ptr(row_pos, _I32, "row_pos", dev), _ptr(row_pos_now, _I32, "row_pos_now", dev), R, int(c),
-        int(max_advance), _ptr(page_table, _I32, "page_table", dev), int(page_table.shape[1]),
-        _ptr(out_slots, _I32, "out_slots", dev), _ptr(out_pos, _I32, "out_pos", dev),
-        _ptr(out_count, _I32, "out_count", dev), int(out_slots.stride(0)), _stream(stream, dev))
-    _check(st, "idx_expand_translate_shared")
+    return (_ptr(sel, _I32, "sel", dev), _ptr(sel_count, _I32, "sel_count", dev), int(k),
+            _ptr(req_row_ptr, _I32, "req_row_ptr", dev), int(req_row_ptr.shape[0]) - 1,
+            _ptr(row_pos, _I32, "row_pos", dev), _ptr(row_pos_now, _I32, "row_pos_now", dev), R, int(c),
+            int(max_advance), _ptr(page_table, _I32, "page_table", dev), int(page_table.shape[1]),
+            _ptr(out_slots, _I32, "out_slots", dev), _ptr(out_pos, _I32, "out_pos", dev),
+            _ptr(out_count, _I32, "out_count", dev), int(out_slots.stride(0)))
+
+
+def idx_expand_translate_shared(sel, sel_count, k, req_row_ptr, row_pos, row_pos_now, c, max_advance, page_table,
+                                out_slots, out_count, out_pos=None, stream=None):
+    """Expansion of a selection reused across draft steps (IndexShare).  See
+    ``idx_expand_translate_shared`` in blockscore.h."""
+    args = _expand_shared_args(sel, sel_count, k, req_row_ptr, row_pos, row_pos_now, c, max_advance, page_table,
+                               out_slots, out_count, out_pos)
+    _check(lib().idx_expand_translate_shared(*args, _stream(stream, sel.device)), "idx_expand_translate_shared")
 
 
 def _select_translate_args(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
@@ -284,6 +290,14 @@ def prepare_topk(scores, row_len, max_len, k, sel, sel_count, workspace=None) ->
                         scores.device)
 
 
+def prepare_expand_shared(sel, sel_count, k, req_row_ptr, row_pos, row_pos_now, c, max_advance, page_table,
+                          out_slots, out_count, out_pos=None) -> PreparedCall:
+    """``idx_expand_translate_shared`` with fixed arguments."""
+    return PreparedCall("idx_expand_translate_shared",
+                        _expand_shared_args(sel, sel_count, k, req_row_ptr, row_pos, row_pos_now, c, max_advance,
+                                            page_table, out_slots, out_count, out_pos), sel.device)
+
+
 def prepare_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
                              out_slots, out_count, out_pos=None, workspace=None) -> PreparedCall:
     """``idx_select_translate`` with fixed arguments."""
@@ -297,5 +311,5 @@ __all__ = [
     "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
     "topk_select_rows", "idx_expand_translate", "idx_expand_translate_shared", "idx_select_translate",
     "status_string", "BlockScoreError",
-    "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate",
+    "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate", "prepare_expand_shared",
 ]

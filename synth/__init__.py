@@ -40,7 +40,13 @@ SEEDS = {
     "qsa_verify_64req": 1003,
     "dsa_decode_16x80k": 1004,
     "qsa_prefill_8k": 1005,
+    "qsa_indexshare_64req": 1006,
 }
+
+# Draft steps of the IndexShare workload; a draft step at most this many
+# positions past the captured row is served by the captured selection.
+INDEXSHARE_DRAFT_STEPS = 3
+INDEXSHARE_MAX_ADVANCE = INDEXSHARE_DRAFT_STEPS + 1
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -238,12 +244,29 @@ def qsa_prefill_8k(seed: int = SEEDS["qsa_prefill_8k"], rows: int = 8192, ctx: i
                              ctx_tokens=[ctx], row_pos_per_req=[list(range(first, ctx))])
 
 
+def qsa_indexshare_64req(seed: int = SEEDS["qsa_indexshare_64req"], B: int = 64,
+                         draft_steps: int = INDEXSHARE_DRAFT_STEPS) -> IndexerInputs:
+    """IndexShare draft step (QSA page, section IndexShare MTP): B requests
+    with contexts drawn as for qsa_verify_64req; one row per request at its
+    last accepted token t0 (the draft-extend row whose selection the draft
+    loop reuses); the cache also holds the draft_steps + 1 positions drafted
+    since, so a draft step at t1 <= t0 + draft_steps + 1 has pages for all of
+    them.  k = 512, c = 4."""
+    rng = np.random.default_rng(seed)
+    L, p = verify_lengths(rng, B)
+    t0 = [int(L[b] + p[b]) - 1 for b in range(B)]
+    ctx = [t + 1 + draft_steps + 1 for t in t0]
+    return build_paged_batch("qsa_indexshare_64req", seed, c=4, k=512,
+                             ctx_tokens=ctx, row_pos_per_req=[[t] for t in t0], rng=rng)
+
+
 WORKLOADS = {
     "qsa_decode_1x8k": qsa_decode_1x8k,
     "topk_8x80k": topk_8x80k,
     "qsa_verify_64req": qsa_verify_64req,
     "dsa_decode_16x80k": dsa_decode_16x80k,
     "qsa_prefill_8k": qsa_prefill_8k,
+    "qsa_indexshare_64req": qsa_indexshare_64req,
 }
 
 

@@ -275,6 +275,26 @@ def test_expand_shared_clamps_the_advance():
     check_expand_exact(slots, pos, oc, rs, rp, rc, tail)
 
 
+def test_expand_shared_full_indexshare_workload():
+    # the benchmark's IndexShare workload: selection by the GPU path at the
+    # captured rows, then the draft step's expansion at +max_advance, exact
+    # against the oracle expanding the same selection
+    import torch
+    from block_scoring_top_amd.pipeline import IndexerPath
+    from synth.device import upload
+    inp = synth.qsa_indexshare_64req()
+    adv = synth.INDEXSHARE_MAX_ADVANCE
+    p = IndexerPath(upload(inp, "cuda"), "decode")
+    p.run()
+    torch.cuda.synchronize()
+    sel, cnt = p.sel.cpu().numpy(), p.sel_count.cpu().numpy()
+    now = inp.row_pos + adv
+    rs, rp, rc = oracle.expand_translate_shared(inp, sel, cnt, now, adv)
+    slots, pos, oc = gu.gpu_expand_shared(inp, sel, cnt, now, adv)
+    tail = now + 1 - 4 * ((inp.row_pos + 1) // 4)
+    check_expand_exact(slots, pos, oc, rs, rp, rc, tail)
+
+
 # ---------------------------------------------------------------------------
 # End to end at the full workload sizes
 # ---------------------------------------------------------------------------
