@@ -37,6 +37,10 @@ def lib():
         L.oracle_expand_translate.restype = C.c_int
         L.oracle_expand_translate_shared.argtypes = [P, P, i32, P, i32, P, P, i32, i32, i32, P, i32, P, P, P, i32]
         L.oracle_expand_translate_shared.restype = C.c_int
+        L.oracle_compress_store.argtypes = [P, P, P, P, i32, i32, P, C.c_double, P, P, P, i32, P, i64, P]
+        L.oracle_compress_store.restype = C.c_int
+        L.oracle_f64_to_bf16.argtypes = [C.c_double]
+        L.oracle_f64_to_bf16.restype = C.c_uint16
         L.oracle_f32_to_f16.argtypes = [C.c_uint32]
         L.oracle_f32_to_f16.restype = C.c_uint16
         L.oracle_key16.argtypes = [C.c_uint16]
@@ -155,6 +159,43 @@ def expand_translate_shared(inp, sel: np.ndarray, count: np.ndarray, row_pos_now
     if st != 0:
         raise OracleError("oracle_expand_translate_shared failed: %d" % st)
     return slots, pos, oc
+
+
+def compress_store(ci, kcache=None, ring=None, ring_pos=None, mrope_pos="inputs"):
+    """Key compression and store (QSA page, section on Qwen sparse attention:
+    4 raw index keys averaged in FP32, normalised, MRoPE-rotated at the
+    block's first token, one bf16 key per block at full_slot/4; the
+    unfinished block's raw keys kept in a 4-slot ring per request).
+
+    Starts from copies of ``kcache`` / ``ring`` / ``ring_pos`` (default: the
+    state held by ``ci``) and returns dict(kcache, ring, ring_pos, exact):
+    the state after the call and, for every cache entry written, its value
+    before bf16 rounding (NaN elsewhere)."""
+    kc = np.array(ci.kcache if kcache is None else kcache, dtype=np.uint16, copy=True, order="C")
+    rg = np.array(ci.ring if ring is None else ring, dtype=np.uint16, copy=True, order="C")
+    rp = np.array(ci.ring_pos if ring_pos is None else ring_pos, dtype=np.int32, copy=True, order="C")
+    mp = ci.mrope_pos if isinstance(mrope_pos, str) else mrope_pos
+    mp = None if mp is None else np.ascontiguousarray(mp, dtype=np.int32)
+    exact = np.full(kc.shape, np.nan, dtype=np.float64)
+    k_raw = np.ascontiguousarray(ci.k_raw, dtype=np.uint16)
+    ptr = np.ascontiguousarray(ci.req_tok_ptr, dtype=np.int32)
+    st0 = np.ascontiguousarray(ci.tok_start, dtype=np.int32)
+    pt = np.ascontiguousarray(ci.page_table, dtype=np.int32)
+    sec = np.ascontiguousarray(ci.sections, dtype=np.int32)
+    st = lib().oracle_compress_store(_p(k_raw) if k_raw.size else None, _p(ptr), _p(st0),
+                                     None if mp is None else _p(mp), ptr.shape[0] - 1,
+                                     int(ci.rotary_dim), _p(sec), float(ci.theta), _p(rg), _p(rp),
+                                     _p(pt), pt.shape[1], _p(kc), int(ci.num_pages), _p(exact))
+    if st != 0:
+        raise OracleError("oracle_compress_store failed: %d" % st)
+    return dict(kcache=kc, ring=rg, ring_pos=rp, exact=exact)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Elementwise double -> bf16 (round to nearest even, one rounding)."""
+    v = np.asarray(x, dtype=np.float64).ravel()
+    f = lib().oracle_f64_to_bf16
+    return np.fromiter((f(float(a)) for a in v), dtype=np.uint16, count=v.size)
 
 
 def pipeline(inp):

@@ -28,6 +28,11 @@
  *                            row's current position (QSA section, IndexShare
  *                            MTP: a captured selection reused across draft
  *                            steps, the positions drafted since appended).
+ *   oracle_compress_store    key compression upstream of the scorer (QSA
+ *                            section: 4 raw index keys averaged in FP32,
+ *                            normalised, rotated with the MRoPE position of
+ *                            the block's first token; a 4-slot raw-key ring
+ *                            per request; full_slot/4 addressing).
  *   oracle_topk_hist         the TopK-V2 steps in the blog's order (FP16 key,
  *                            10-bit bins, threshold bin, direct emission,
  *                            exact refinement of the boundary bin), written
@@ -281,6 +286,130 @@ int oracle_expand_translate_shared(const int32_t* sel, const int32_t* sel_count,
     return OR_ERR_ARG;
   return expand_rows(sel, sel_count, k, req_row_ptr, num_req, row_pos, row_pos_now, max_advance, c, page_table,
                      pt_stride, out_slots, out_pos, out_count, ld_out);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Double -> bf16 bit pattern, round to nearest, ties to even, in one step   */
+/* (a pass through FP32 would round twice); overflow -> infinity.  A value   */
+/* in [2^e, 2^(e+1)) has the quantum 2^(e-7); below 2^-126 the quantum is    */
+/* 2^-133 (bf16 subnormals).                                                 */
+/* ------------------------------------------------------------------------ */
+uint16_t oracle_f64_to_bf16(double x) {
+  if (isnan(x)) return 0x7FC0u;
+  const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  const double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+  int e = ilogb(a);
+  if (e < -126) e = -126;
+  const double quantum = ldexp(1.0, e - 7);
+  const double r = nearbyint(a / quantum) * quantum; /* a / quantum is exact */
+  if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+  const float f = (float)r; /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(sign | (u >> 16));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Key compression and store, the step just upstream of the scorer (QSA      */
+/* section: the indexer's one shared key head; every 4 raw index keys are    */
+/* averaged in FP32, normalised and rotated with the MRoPE position of their */
+/* first token into one bf16 compressed key; the raw keys of a request's     */
+/* unfinished block wait in a 4-slot ring; the compressed cache is addressed */
+/* page-aligned at full_slot/4).                                             */
+/*                                                                           */
+/* Readings, where the page names the steps only:                            */
+/*  - a request's new tokens are taken in position order.  The token at      */
+/*    position p goes to ring slot p mod 4; when p mod 4 == 0 its MRoPE      */
+/*    position (t, h, w) becomes the ring's block position; when             */
+/*    p mod 4 == 3 the ring's 4 keys form block p/4, stored at               */
+/*    page_table[b][(4j)/64] * 16 + j mod 16;                                */
+/*  - average: ((k0 + k1) + k2) + k3 in FP32, times 0.25 (exact);            */
+/*  - normalise: divide by the L2 norm; a zero mean stays zero;              */
+/*  - rotate: rotate-half pairs (i, i + rot/2) over the first rot dims, the  */
+/*    other dims pass through.  Pair i has the frequency theta^(-2i/rot) and */
+/*    takes its position from component t when i < sec[0], h when            */
+/*    i < sec[0] + sec[1], w otherwise (contiguous MRoPE sections; a text    */
+/*    token has t = h = w = its position, which makes the layout moot).      */
+/*    out_i = y_i cos a - y_{i+rot/2} sin a,                                 */
+/*    out_{i+rot/2} = y_{i+rot/2} cos a + y_i sin a;                         */
+/*  - the result is rounded once to bf16 (nearest, ties to even).           */
+/* Normalisation and rotation run in double precision from the FP32 mean;    */
+/* `exact` (optional, the shape of kcache) receives the unrounded values of  */
+/* every key written.                                                        */
+/*                                                                           */
+/* k_raw [T][128] bf16: the new tokens; request b owns tokens                */
+/* req_tok_ptr[b] .. req_tok_ptr[b+1]-1 at positions tok_start[b] + i.       */
+/* mrope_pos [T][3] or NULL (text positions).  ring [num_req][4][128] bf16,  */
+/* ring_pos [num_req][3] (required with mrope_pos; read only then).          */
+/* ------------------------------------------------------------------------ */
+static void compress_block(const uint16_t* ring4, const int32_t* P, int32_t rot, const int32_t* sec,
+                           double theta, double* out) {
+  float mean[OR_DIM];
+  for (int d = 0; d < OR_DIM; ++d) {
+    float s = (float)bf16_value(ring4[d]);
+    s += (float)bf16_value(ring4[OR_DIM + d]);
+    s += (float)bf16_value(ring4[2 * OR_DIM + d]);
+    s += (float)bf16_value(ring4[3 * OR_DIM + d]);
+    mean[d] = s * 0.25f;
+  }
+  double ss = 0.0;
+  for (int d = 0; d < OR_DIM; ++d) ss += (double)mean[d] * (double)mean[d];
+  const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+  double y[OR_DIM];
+  for (int d = 0; d < OR_DIM; ++d) y[d] = (double)mean[d] * inv;
+  const int32_t half = rot / 2;
+  for (int d = 0; d < OR_DIM; ++d) out[d] = y[d];
+  for (int32_t i = 0; i < half; ++i) {
+    const int comp = i < sec[0] ? 0 : (i < sec[0] + sec[1] ? 1 : 2);
+    const double angle = (double)P[comp] * pow(theta, -2.0 * (double)i / (double)rot);
+    const double ca = cos(angle), sa = sin(angle);
+    out[i] = y[i] * ca - y[i + half] * sa;
+    out[i + half] = y[i + half] * ca + y[i] * sa;
+  }
+}
+
+int oracle_compress_store(const uint16_t* k_raw, const int32_t* req_tok_ptr, const int32_t* tok_start,
+                          const int32_t* mrope_pos, int32_t num_req,
+                          int32_t rotary_dim, const int32_t* sections, double theta,
+                          uint16_t* ring, int32_t* ring_pos,
+                          const int32_t* page_table, int32_t pt_stride,
+                          uint16_t* kcache, int64_t num_pages, double* exact) {
+  if (num_req < 0 || rotary_dim < 0 || rotary_dim > OR_DIM || (rotary_dim & 1)) return OR_ERR_ARG;
+  if (sections[0] < 0 || sections[1] < 0 || sections[2] < 0 ||
+      sections[0] + sections[1] + sections[2] != rotary_dim / 2)
+    return OR_ERR_ARG;
+  if (!(theta > 0.0) || isinf(theta) || (mrope_pos && !ring_pos)) return OR_ERR_ARG;
+  const int32_t per_page = OR_PAGE / 4;
+  int status = OR_OK;
+  for (int32_t b = 0; b < num_req; ++b) {
+    const int32_t s = tok_start[b], n = req_tok_ptr[b + 1] - req_tok_ptr[b];
+    if (s < 0 || n < 0) { status = OR_ERR_DATA; continue; }
+    uint16_t* ring4 = ring + (int64_t)b * 4 * OR_DIM;
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t p = s + i;
+      const int64_t tok = (int64_t)req_tok_ptr[b] + i;
+      memcpy(ring4 + (p % 4) * OR_DIM, k_raw + tok * OR_DIM, sizeof(uint16_t) * OR_DIM);
+      if (p % 4 == 0 && ring_pos)
+        for (int u = 0; u < 3; ++u) ring_pos[(int64_t)b * 3 + u] = mrope_pos ? mrope_pos[tok * 3 + u] : p;
+      if (p % 4 != 3) continue;
+      const int32_t j = p / 4;
+      int32_t P[3];
+      for (int u = 0; u < 3; ++u) P[u] = mrope_pos ? ring_pos[(int64_t)b * 3 + u] : 4 * j;
+      if ((4 * (int64_t)j) / OR_PAGE >= pt_stride) { status = OR_ERR_DATA; continue; }
+      const int32_t page = page_table[(int64_t)b * pt_stride + (4 * j) / OR_PAGE];
+      if (page < 0 || page >= num_pages) { status = OR_ERR_DATA; continue; }
+      double out[OR_DIM];
+      compress_block(ring4, P, rotary_dim, sections, theta, out);
+      const int64_t slot = (int64_t)page * per_page + j % per_page;
+      for (int d = 0; d < OR_DIM; ++d) {
+        kcache[slot * OR_DIM + d] = oracle_f64_to_bf16(out[d]);
+        if (exact) exact[slot * OR_DIM + d] = out[d];
+      }
+    }
+  }
+  return status;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -41,7 +41,18 @@ SEEDS = {
     "dsa_decode_16x80k": 1004,
     "qsa_prefill_8k": 1005,
     "qsa_indexshare_64req": 1006,
+    "qsa_compress_prefill_8k": 1007,
+    "qsa_compress_decode_64req": 1008,
 }
+
+# Rotary parameters of the compressed index key.  The pages name an MRoPE
+# rotation at the block's first token and nothing more; the values taken are
+# Qwen2-VL's: the whole 128-dim key rotated, its 64 frequency pairs split
+# 16 / 24 / 24 over the temporal / height / width position components, base
+# 1,000,000.
+ROPE_DIM = 128
+MROPE_SECTIONS = (16, 24, 24)
+ROPE_THETA = 1.0e6
 
 # Draft steps of the IndexShare workload; a draft step at most this many
 # positions past the captured row is served by the captured selection.
@@ -112,6 +123,113 @@ class ScoreRows:
     @property
     def max_len(self) -> int:
         return int(self.scores.shape[1])
+
+
+@dataclasses.dataclass
+class CompressInputs:
+    """New raw index keys of a batch of requests, to be compressed into the
+    c = 4 index cache, with the cache and ring state before the call."""
+
+    name: str
+    k_raw: np.ndarray                 # uint16 [T][128] bf16, tokens of a request contiguous
+    req_tok_ptr: np.ndarray           # int32 [B+1]
+    tok_start: np.ndarray             # int32 [B], position of each request's first new token
+    mrope_pos: Optional[np.ndarray]   # int32 [T][3] (t, h, w) or None for text positions
+    ring: np.ndarray                  # uint16 [B][4][128] bf16
+    ring_pos: np.ndarray              # int32 [B][3]
+    page_table: np.ndarray            # int32 [B][pt_stride]
+    kcache: np.ndarray                # uint16 [num_pages*16][128] bf16
+    num_pages: int
+    rotary_dim: int
+    sections: tuple
+    theta: float
+    seed: int
+
+    @property
+    def num_req(self) -> int:
+        return int(self.req_tok_ptr.shape[0] - 1)
+
+    @property
+    def num_tok(self) -> int:
+        return int(self.k_raw.shape[0])
+
+    @property
+    def max_tok(self) -> int:
+        """Host-side bound on new tokens per request."""
+        return int(np.max(np.diff(self.req_tok_ptr), initial=0))
+
+    @property
+    def pt_stride(self) -> int:
+        return int(self.page_table.shape[1])
+
+
+def mrope_positions(tokens: np.ndarray, images=()) -> np.ndarray:
+    """(t, h, w) position components of token indices ``tokens`` for a
+    sequence whose image spans are ``images`` = [(first token, grid g), ...]
+    in order.  Text tokens carry t = h = w; an image of g x g tokens shares
+    one t, its rows and columns add to h and w, and the text after it resumes
+    g positions later."""
+    x = np.asarray(tokens, dtype=np.int64)
+    out = np.empty((x.shape[0], 3), dtype=np.int64)
+    shift = np.zeros_like(x)
+    in_img = np.zeros(x.shape[0], dtype=bool)
+    for a, g in images:
+        inside = (x >= a) & (x < a + g * g)
+        base = a - shift[inside]
+        off = x[inside] - a
+        out[inside, 0] = base
+        out[inside, 1] = base + off // g
+        out[inside, 2] = base + off % g
+        in_img |= inside
+        shift[x >= a + g * g] += g * g - g
+    text = ~in_img
+    out[text, :] = (x[text] - shift[text])[:, None]
+    return out.astype(np.int32)
+
+
+def build_compress_batch(name: str, seed: int, starts, counts, ctx_tokens,
+                         images=None, text_positions: bool = False,
+                         rng: Optional[np.random.Generator] = None,
+                         identity_pages: bool = False,
+                         rotary_dim: int = ROPE_DIM, sections=MROPE_SECTIONS,
+                         theta: float = ROPE_THETA) -> CompressInputs:
+    """Lay out one compression call: request ``b`` appends ``counts[b]`` new
+    tokens at positions ``starts[b]`` ... and owns ``ceil(ctx_tokens[b]/64)``
+    pages (a seeded permutation of all pages).  Raw keys ~N(0,1) rounded to
+    bf16.  The ring holds raw keys of the tokens of the block the first new
+    token falls in (random keys in its stale slots) and the MRoPE position of
+    that block's first token; the cache starts filled with normalised random
+    keys.  ``images[b]`` lists request ``b``'s image spans; with
+    ``text_positions`` the call passes no MRoPE positions at all."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    B = len(starts)
+    images = images if images is not None else [()] * B
+    pages = [max(1, -(-int(t) // PAGE_TOKENS)) for t in ctx_tokens]
+    total = int(sum(pages))
+    perm = np.arange(total, dtype=np.int64) if identity_pages else rng.permutation(total)
+    pt = np.full((B, max(pages)), -1, dtype=np.int32)
+    off = 0
+    for b, np_b in enumerate(pages):
+        pt[b, :np_b] = perm[off:off + np_b]
+        off += np_b
+    ptr = np.zeros(B + 1, dtype=np.int32)
+    ptr[1:] = np.cumsum(counts)
+    T = int(ptr[-1])
+    k_raw = f32_to_bf16_bits(_normal_f32(rng, (max(T, 1), DIM)))[:T]
+    mpos = np.zeros((T, 3), dtype=np.int32)
+    ring_pos = rng.integers(0, 1 << 20, size=(B, 3)).astype(np.int32)
+    for b in range(B):
+        s, n = int(starts[b]), int(counts[b])
+        mpos[ptr[b]:ptr[b + 1]] = mrope_positions(np.arange(s, s + n), images[b])
+        ring_pos[b] = mrope_positions(np.array([s - s % 4]), images[b])[0]
+    ring = f32_to_bf16_bits(_normal_f32(rng, (B * 4, DIM))).reshape(B, 4, DIM)
+    kcache = draw_normalised_keys(rng, total * (PAGE_TOKENS // 4))
+    return CompressInputs(name=name, k_raw=k_raw, req_tok_ptr=ptr,
+                          tok_start=np.asarray(starts, dtype=np.int32),
+                          mrope_pos=None if text_positions else mpos,
+                          ring=ring, ring_pos=ring_pos, page_table=pt, kcache=kcache,
+                          num_pages=total, rotary_dim=int(rotary_dim),
+                          sections=tuple(int(v) for v in sections), theta=float(theta), seed=seed)
 
 
 def _normal_f32(rng: np.random.Generator, shape, chunk_rows: int = 1 << 16) -> np.ndarray:
@@ -260,6 +378,29 @@ def qsa_indexshare_64req(seed: int = SEEDS["qsa_indexshare_64req"], B: int = 64,
                              ctx_tokens=ctx, row_pos_per_req=[[t] for t in t0], rng=rng)
 
 
+def qsa_compress_prefill_8k(seed: int = SEEDS["qsa_compress_prefill_8k"], chunk: int = 8192,
+                            ctx: int = 65536) -> CompressInputs:
+    """Key compression for the prefill chunk of qsa_prefill_8k: 1 request,
+    ``chunk`` new tokens at positions ctx - chunk ... ctx - 1 (2048 complete
+    blocks), explicit MRoPE positions with one 64 x 64 image early in the
+    context and one 32 x 32 image inside the chunk."""
+    first = ctx - chunk
+    images = [((ctx // 4, 64), (first + chunk // 4 + 2, 32))]
+    return build_compress_batch("qsa_compress_prefill_8k", seed, [first], [chunk], [ctx],
+                                images=images)
+
+
+def qsa_compress_decode_64req(seed: int = SEEDS["qsa_compress_decode_64req"], B: int = 64) -> CompressInputs:
+    """Key compression in a decode step: B requests with contexts drawn as for
+    qsa_verify_64req, each appending the key of its newest token (about a
+    quarter of them complete a block); text positions."""
+    rng = np.random.default_rng(seed)
+    L, p = verify_lengths(rng, B)
+    ctx = [int(L[b] + p[b]) for b in range(B)]
+    return build_compress_batch("qsa_compress_decode_64req", seed, [c - 1 for c in ctx], [1] * B, ctx,
+                                text_positions=True, rng=rng)
+
+
 WORKLOADS = {
     "qsa_decode_1x8k": qsa_decode_1x8k,
     "topk_8x80k": topk_8x80k,
@@ -267,6 +408,8 @@ WORKLOADS = {
     "dsa_decode_16x80k": dsa_decode_16x80k,
     "qsa_prefill_8k": qsa_prefill_8k,
     "qsa_indexshare_64req": qsa_indexshare_64req,
+    "qsa_compress_prefill_8k": qsa_compress_prefill_8k,
+    "qsa_compress_decode_64req": qsa_compress_decode_64req,
 }
 
 
