@@ -187,6 +187,8 @@ def run_workload(name, K, warmup, dev, fused=True):
                              "algorithmic_bytes": alg, "avg_us": round(t_topk * 1e3, 2)}}
     if name == "qsa_indexshare_64req":
         return run_indexshare(name, inp, K, warmup, dev, stream)
+    if isinstance(inp, synth.CompressInputs):
+        return run_compress(name, inp, K, warmup, dev, stream)
     scorer = "prefill" if name == "qsa_prefill_8k" else "decode"
     path = IndexerPath(upload(inp, dev), scorer)
     if fused:
@@ -262,6 +264,40 @@ def run_indexshare(name, inp, K, warmup, dev, stream):
                          "algorithmic_bytes": alg, "avg_us": round(t_call * 1e3, 2)}}
 
 
+def run_compress(name, ci, K, warmup, dev, stream):
+    """Key compression into the c = 4 cache: one idx_compress_store call over
+    the batch's new raw keys (each step recomputes the same blocks)."""
+    import numpy as np
+
+    import block_scoring_top_amd as bst
+    from synth.device import upload_compress
+
+    d = upload_compress(ci, dev)
+    call = bst.prepare_compress_store(*d.args())
+    ms, t_call = time_steps([call], K, warmup, stream)
+    counts = np.diff(ci.req_tok_ptr).astype(np.int64)
+    starts = ci.tok_start.astype(np.int64)
+    blocks = (starts + counts) // 4 - starts // 4
+    straddle = np.where((blocks > 0) & (starts % 4 > 0), starts % 4, 0)
+    T = ci.num_tok
+    alg = (T * 256 + (T * 12 if ci.mrope_pos is not None else 0)      # raw keys and MRoPE positions in
+           + int(straddle.sum()) * 256 + ci.num_req * 8                  # ring entries of straddling blocks
+           + int(blocks.sum()) * (256 + 4)                               # compressed keys out, page ids in
+           + int(np.minimum(counts, 4).sum()) * 256 + ci.num_req * 12)   # ring and ring positions out
+    ach = alg / (t_call * 1e-3) / 1e9
+    log(f"{name}: {ms * 1e3:.1f} us/step ({int(blocks.sum())} compressed keys from {T} new tokens)")
+    return {"_inp": ci, "rows_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+            "config": {"workload": name, "requests": ci.num_req, "new_tokens": T,
+                       "compressed_keys": int(blocks.sum()), "rotary_dim": ci.rotary_dim,
+                       "mrope_sections": list(ci.sections), "theta": ci.theta,
+                       "mrope": "explicit" if ci.mrope_pos is not None else "text positions",
+                       "steps": "key compression and store (rows = new tokens)"},
+            "kernels_us": {"compress": round(t_call * 1e3, 2)},
+            "roofline": {"bound": "latency", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "compress_kernel",
+                         "algorithmic_bytes": alg, "avg_us": round(t_call * 1e3, 2)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,7 +339,7 @@ def main():
     extra = {}
     if args.all:
         for name in synth.WORKLOADS:
-            if name == args.workload or name.startswith("qsa_compress"):
+            if name == args.workload:
                 continue
             r = run_workload(name, args.steps, args.warmup, dev, fused=not args.unfused)
             r.pop("_inp")

@@ -61,6 +61,9 @@ def lib():
         L.idx_select_translate.argtypes = [P, i64, P, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P, P, i32,
                                            P, C.c_size_t, P]
         L.idx_select_translate.restype = C.c_int
+        L.idx_compress_store.argtypes = [P, i32, P, P, P, i32, i32, i32, i32, i32, i32, C.c_double, P, P, P, i32,
+                                         P, i64, P]
+        L.idx_compress_store.restype = C.c_int
         L.bs_status_string.argtypes = [C.c_int]
         L.bs_status_string.restype = C.c_char_p
         L.bs_abi_version.argtypes = []
@@ -258,6 +261,41 @@ def idx_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, c, p
     _check(lib().idx_select_translate(*args, _stream(stream, scores.device)), "idx_select_translate")
 
 
+def _compress_args(k_raw, req_tok_ptr, tok_start, mrope_pos, max_tok, rotary_dim, sections, theta, ring,
+                   ring_pos, page_table, kcache, num_pages):
+    """Checked argument tuple of an ``idx_compress_store`` call (all but the stream)."""
+    dev = k_raw.device
+    T = int(k_raw.shape[0])
+    B = int(req_tok_ptr.shape[0]) - 1
+    if k_raw.dim() != 2 or k_raw.shape[1] != 128:
+        raise ValueError("k_raw must be [num_tok, 128]")
+    if tok_start.numel() != B or ring.shape != (B, 4, 128):
+        raise ValueError("tok_start must hold num_req entries and ring be [num_req, 4, 128]")
+    if mrope_pos is not None and mrope_pos.shape != (T, 3):
+        raise ValueError("mrope_pos must be [num_tok, 3]")
+    if ring_pos is not None and ring_pos.shape != (B, 3):
+        raise ValueError("ring_pos must be [num_req, 3]")
+    if kcache.dim() != 2 or kcache.shape[1] != 128 or kcache.shape[0] < 16 * int(num_pages):
+        raise ValueError("kcache must be [>= num_pages * 16, 128]")
+    sec = [int(v) for v in sections]
+    if len(sec) != 3:
+        raise ValueError("sections must hold 3 entries (t, h, w)")
+    return (_ptr(k_raw, _BF16, "k_raw", dev), T, _ptr(req_tok_ptr, _I32, "req_tok_ptr", dev),
+            _ptr(tok_start, _I32, "tok_start", dev), _ptr(mrope_pos, _I32, "mrope_pos", dev), B, int(max_tok),
+            int(rotary_dim), sec[0], sec[1], sec[2], float(theta), _ptr(ring, _BF16, "ring", dev),
+            _ptr(ring_pos, _I32, "ring_pos", dev), _ptr(page_table, _I32, "page_table", dev),
+            int(page_table.shape[1]), _ptr(kcache, _BF16, "kcache", dev), int(num_pages))
+
+
+def idx_compress_store(k_raw, req_tok_ptr, tok_start, mrope_pos, max_tok, rotary_dim, sections, theta, ring,
+                       ring_pos, page_table, kcache, num_pages, stream=None):
+    """Compress new raw index keys into the c = 4 key cache (and update the
+    rings).  See ``idx_compress_store`` in blockscore.h."""
+    args = _compress_args(k_raw, req_tok_ptr, tok_start, mrope_pos, max_tok, rotary_dim, sections, theta, ring,
+                          ring_pos, page_table, kcache, num_pages)
+    _check(lib().idx_compress_store(*args, _stream(stream, k_raw.device)), "idx_compress_store")
+
+
 class PreparedCall:
     """One C call with its arguments checked and marshalled once (the tensors
     behind the pointers must outlive it); ``__call__`` adds the stream and
@@ -313,3 +351,11 @@ __all__ = [
     "status_string", "BlockScoreError",
     "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate", "prepare_expand_shared",
 ]
+
+
+def prepare_compress_store(k_raw, req_tok_ptr, tok_start, mrope_pos, max_tok, rotary_dim, sections, theta, ring,
+                           ring_pos, page_table, kcache, num_pages) -> PreparedCall:
+    """``idx_compress_store`` with fixed arguments."""
+    return PreparedCall("idx_compress_store",
+                        _compress_args(k_raw, req_tok_ptr, tok_start, mrope_pos, max_tok, rotary_dim, sections,
+                                       theta, ring, ring_pos, page_table, kcache, num_pages), k_raw.device)

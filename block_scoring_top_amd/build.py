@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libblockscore.so")
-SOURCES = ["api.hip", "score_decode.hip", "score_prefill.hip", "topk.hip", "expand.hip"]
+SOURCES = ["api.hip", "score_decode.hip", "score_prefill.hip", "topk.hip", "expand.hip", "compress.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

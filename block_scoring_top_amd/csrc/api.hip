@@ -2,6 +2,8 @@
 //
 // Nothing here allocates, frees or synchronises.  Every check below runs on
 // host-side values only; device data is never read back.
+#include <cmath>
+
 #include "../../include/blockscore.h"
 #include "kernels.h"
 
@@ -135,6 +137,25 @@ BS_EXPORT int idx_select_translate(const float* scores, int64_t ld_scores, const
   return bs::launch_select_translate(scores, ld_scores, row_len, num_rows, max_len, k, req_row_ptr, num_req,
                                      row_pos, c, page_table, pt_stride, sel, sel_count, out_slots, out_pos,
                                      out_count, ld_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+BS_EXPORT int idx_compress_store(const uint16_t* k_raw, int32_t num_tok, const int32_t* req_tok_ptr,
+                                 const int32_t* tok_start, const int32_t* mrope_pos, int32_t num_req,
+                                 int32_t max_tok, int32_t rotary_dim, int32_t sec_t, int32_t sec_h, int32_t sec_w,
+                                 double theta, uint16_t* ring, int32_t* ring_pos, const int32_t* page_table,
+                                 int32_t pt_stride, uint16_t* kcache, int64_t num_pages, void* stream) {
+  if (num_req < 0 || num_tok < 0 || max_tok < 0 || num_pages < 0 || num_req > 65535) return BS_ERR_ARG;
+  if (max_tok > num_tok) return BS_ERR_ARG;
+  if (rotary_dim < 0 || rotary_dim > BS_DIM || (rotary_dim & 1)) return BS_ERR_ARG;
+  if (sec_t < 0 || sec_h < 0 || sec_w < 0 || sec_t + sec_h + sec_w != rotary_dim / 2) return BS_ERR_ARG;
+  if (!(theta > 0.0) || !std::isfinite(theta)) return BS_ERR_ARG;
+  if (num_req == 0 || num_tok == 0 || max_tok == 0) return BS_OK;
+  if (!k_raw || !req_tok_ptr || !tok_start || !ring || !page_table || !kcache) return BS_ERR_NULL;
+  if (mrope_pos && !ring_pos) return BS_ERR_NULL;
+  if (pt_stride < 1 || num_pages < 1) return BS_ERR_ARG;
+  return bs::launch_compress(k_raw, num_tok, req_tok_ptr, tok_start, mrope_pos, num_req, max_tok, rotary_dim,
+                             sec_t, sec_h, theta, ring, ring_pos, page_table, pt_stride, kcache, num_pages,
+                             static_cast<hipStream_t>(stream));
 }
 
 BS_EXPORT const char* bs_status_string(int status) {

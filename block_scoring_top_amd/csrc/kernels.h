@@ -43,4 +43,11 @@ int launch_expand(const int32_t* sel, const int32_t* sel_count, int32_t k,
                   int32_t* out_slots, int32_t* out_pos, int32_t* out_count,
                   int32_t ld_out, hipStream_t stream);
 
+// Key compression into the c = 4 cache; arguments validated by the caller.
+int launch_compress(const uint16_t* k_raw, int32_t num_tok, const int32_t* req_tok_ptr, const int32_t* tok_start,
+                    const int32_t* mrope_pos, int32_t num_req, int32_t max_tok, int32_t rotary_dim,
+                    int32_t sec_t, int32_t sec_h, double theta, uint16_t* ring, int32_t* ring_pos,
+                    const int32_t* page_table, int32_t pt_stride, uint16_t* kcache, int64_t num_pages,
+                    hipStream_t stream);
+
 }  // namespace bs

@@ -5,9 +5,10 @@
  *   1. score   - idx_score_decode / idx_score_prefill
  *   2. select  - topk_select_rows
  *   3. expand  - idx_expand_translate
- * plus idx_select_translate (steps 2 and 3 in one kernel) and
+ * plus idx_select_translate (steps 2 and 3 in one kernel),
  * idx_expand_translate_shared (step 3 for a selection reused across
- * speculative draft steps).
+ * speculative draft steps) and idx_compress_store (the step before 1: raw
+ * index keys compressed into the c = 4 key cache).
  *
  * Sources (pages on the subject):
  *   [QSA]   "Qwen3.8-Flash-Next Day-0 in SGLang" (theainews.cc), section on Qwen
@@ -246,6 +247,61 @@ int idx_select_translate(const float* scores, int64_t ld_scores, const int32_t* 
                          int32_t* sel, int32_t* sel_count,
                          int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * idx_compress_store - compression of new raw index keys into the c = 4 key
+ * cache the scorers read [QSA: the indexer's one shared key head; each 4 raw
+ * index keys are averaged in FP32, normalised and rotated with the MRoPE
+ * position of their first token into one bf16 compressed key; the raw keys
+ * of a request's unfinished block wait in a 4-slot ring; page-aligned
+ * full_slot/4 addressing].
+ *
+ * Request b appends tokens req_tok_ptr[b] .. req_tok_ptr[b+1]-1 of k_raw at
+ * consecutive positions tok_start[b], tok_start[b]+1, ...  The result is that
+ * of taking the tokens in position order: the token at position p is written
+ * to ring slot p mod 4 (and, when p mod 4 == 0, its MRoPE position to
+ * ring_pos[b]); when p mod 4 == 3 the ring's 4 keys form block j = p/4:
+ *   mean = ((k0 + k1) + k2) + k3 in FP32, times 0.25;
+ *   y    = mean / ||mean||_2 (a zero mean gives zeros);
+ *   rotate-half over the first rotary_dim dims: pair i < rotary_dim/2 joins
+ *        dims i and i + rotary_dim/2 and turns by P * theta^(-2i/rotary_dim),
+ *        P being the t, h or w component of the block position for i in the
+ *        first sec_t, the next sec_h or the last sec_w pairs; other dims pass;
+ *   the result, rounded to bf16 (nearest even), is stored at compressed slot
+ *        page_table[b][(4j)/64] * 16 + j mod 16 (kcache layout above, c = 4).
+ * The block position is the MRoPE position of token 4j (ring_pos[b] when that
+ * token came in an earlier call).  Normalisation and rotation run in FP32 with
+ * FP64 angles: each element is within 2^-17 of the exact value of these steps
+ * before its bf16 rounding.
+ *
+ *   k_raw        [num_tok][128] bf16, the new raw keys.
+ *   req_tok_ptr  [num_req + 1] int32, non-decreasing, last entry <= num_tok.
+ *   tok_start    [num_req] int32 >= 0, position of each request's first new
+ *                token; the ring must hold that request's tokens
+ *                4*floor(tok_start/4) .. tok_start-1 from earlier calls.
+ *   mrope_pos    [num_tok][3] int32 (t, h, w) of each new token, or NULL for
+ *                text positions (t = h = w = the token position).
+ *   max_tok      host-side bound on the new tokens of any request (sizes the
+ *                grid; a request with more is cut to max_tok), <= num_tok.
+ *   rotary_dim   0 .. 128, even; sec_t + sec_h + sec_w == rotary_dim / 2.
+ *   theta        rotary base, finite and > 0.
+ *   ring         [num_req][4][128] bf16, read and written.
+ *   ring_pos     [num_req][3] int32, read and written; required when
+ *                mrope_pos is given, may be NULL otherwise.
+ *   page_table   as above; kcache [num_pages * 16][128] bf16, written only at
+ *                the slots of completed blocks whose page id is in range.
+ * Calls that share a ring or cache entries must not overlap in time.
+ * Returns BS_OK (also when num_req, num_tok or max_tok is 0), BS_ERR_NULL,
+ * BS_ERR_ARG (negative counts, num_req > 65535, max_tok > num_tok, bad
+ * rotary_dim, sections or theta, pt_stride < 1, num_pages < 1) or
+ * BS_ERR_LAUNCH.
+ */
+int idx_compress_store(const uint16_t* k_raw, int32_t num_tok, const int32_t* req_tok_ptr,
+                       const int32_t* tok_start, const int32_t* mrope_pos, int32_t num_req, int32_t max_tok,
+                       int32_t rotary_dim, int32_t sec_t, int32_t sec_h, int32_t sec_w, double theta,
+                       uint16_t* ring, int32_t* ring_pos,
+                       const int32_t* page_table, int32_t pt_stride, uint16_t* kcache, int64_t num_pages,
+                       void* stream);
 
 /* bs_status_string - a static, human-readable name for a status code. */
 const char* bs_status_string(int status);

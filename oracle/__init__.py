@@ -161,7 +161,7 @@ def expand_translate_shared(inp, sel: np.ndarray, count: np.ndarray, row_pos_now
     return slots, pos, oc
 
 
-def compress_store(ci, kcache=None, ring=None, ring_pos=None, mrope_pos="inputs"):
+def compress_store(ci, kcache=None, ring=None, ring_pos=None, mrope_pos="inputs", strict=True):
     """Key compression and store (QSA page, section on Qwen sparse attention:
     4 raw index keys averaged in FP32, normalised, MRoPE-rotated at the
     block's first token, one bf16 key per block at full_slot/4; the
@@ -170,7 +170,9 @@ def compress_store(ci, kcache=None, ring=None, ring_pos=None, mrope_pos="inputs"
     Starts from copies of ``kcache`` / ``ring`` / ``ring_pos`` (default: the
     state held by ``ci``) and returns dict(kcache, ring, ring_pos, exact):
     the state after the call and, for every cache entry written, its value
-    before bf16 rounding (NaN elsewhere)."""
+    before bf16 rounding (NaN elsewhere).  With ``strict=False`` blocks whose
+    page id is out of range (or requests with a negative start) are skipped
+    instead of raising."""
     kc = np.array(ci.kcache if kcache is None else kcache, dtype=np.uint16, copy=True, order="C")
     rg = np.array(ci.ring if ring is None else ring, dtype=np.uint16, copy=True, order="C")
     rp = np.array(ci.ring_pos if ring_pos is None else ring_pos, dtype=np.int32, copy=True, order="C")
@@ -186,7 +188,7 @@ def compress_store(ci, kcache=None, ring=None, ring_pos=None, mrope_pos="inputs"
                                      None if mp is None else _p(mp), ptr.shape[0] - 1,
                                      int(ci.rotary_dim), _p(sec), float(ci.theta), _p(rg), _p(rp),
                                      _p(pt), pt.shape[1], _p(kc), int(ci.num_pages), _p(exact))
-    if st != 0:
+    if st != 0 and (strict or st != -5):
         raise OracleError("oracle_compress_store failed: %d" % st)
     return dict(kcache=kc, ring=rg, ring_pos=rp, exact=exact)
 

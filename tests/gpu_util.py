@@ -9,7 +9,7 @@ import torch
 
 import block_scoring_top_amd as bst
 from block_scoring_top_amd.pipeline import IndexerPath
-from synth.device import upload
+from synth.device import upload, upload_compress
 
 
 def say(msg: str):
@@ -98,3 +98,27 @@ def gpu_scores(inp, scorer: str = "decode", ld: int | None = None):
 def pending_counts(inp) -> np.ndarray:
     t = inp.row_pos.astype(np.int64)
     return (t + 1 - inp.c * ((t + 1) // inp.c)).astype(np.int32)
+
+
+def gpu_compress(ci, kcache=None, ring=None, ring_pos=None, max_tok=None):
+    """Runs idx_compress_store on ``ci`` starting from the given (default:
+    ci's) cache and ring state; returns dict(kcache, ring, ring_pos)."""
+    say(f"compress {getattr(ci, 'name', '?')} requests={ci.num_req} tokens={ci.num_tok} max_tok={ci.max_tok} "
+        f"rot={ci.rotary_dim} sections={ci.sections} mrope={'yes' if ci.mrope_pos is not None else 'text'}")
+    d = upload_compress(ci, "cuda")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    if kcache is not None:
+        d.kcache = bf(kcache)
+    if ring is not None:
+        d.ring = bf(ring)
+    if ring_pos is not None:
+        d.ring_pos = torch.from_numpy(np.ascontiguousarray(ring_pos, dtype=np.int32)).cuda()
+    if max_tok is not None:
+        d.max_tok = int(max_tok)
+    bst.idx_compress_store(*d.args())
+    torch.cuda.synchronize()
+    return dict(kcache=d.kcache.cpu().numpy().view(np.uint16), ring=d.ring.cpu().numpy().view(np.uint16),
+                ring_pos=d.ring_pos.cpu().numpy())
+

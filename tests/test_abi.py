@@ -184,3 +184,34 @@ def test_expand_shared_validation():
     assert _expand_shared(pt_stride=0) == BS_ERR_ARG
     for k in ("sel", "cnt", "ptr", "pos", "now", "pt", "slots", "ocnt"):
         assert _expand_shared(**{k: NULL}) == BS_ERR_NULL, k
+
+
+def _compress(**kw):
+    a = dict(k_raw=FAKE, num_tok=8, ptr=FAKE, start=FAKE, mpos=NULL, num_req=1, max_tok=8, rot=128, st=16, sh=24,
+             sw=24, theta=1.0e6, ring=FAKE, ring_pos=NULL, pt=FAKE, pt_stride=1, kc=FAKE, num_pages=1, stream=NULL)
+    a.update(kw)
+    return bst.lib().idx_compress_store(a["k_raw"], a["num_tok"], a["ptr"], a["start"], a["mpos"], a["num_req"],
+                                        a["max_tok"], a["rot"], a["st"], a["sh"], a["sw"], a["theta"], a["ring"],
+                                        a["ring_pos"], a["pt"], a["pt_stride"], a["kc"], a["num_pages"],
+                                        a["stream"])
+
+
+def test_compress_validation():
+    assert _compress(num_req=0) == BS_OK
+    assert _compress(num_tok=0, max_tok=0) == BS_OK
+    assert _compress(max_tok=0) == BS_OK
+    assert _compress(max_tok=9) == BS_ERR_ARG              # more than num_tok
+    assert _compress(num_req=-1) == BS_ERR_ARG
+    assert _compress(num_req=65536) == BS_ERR_ARG
+    assert _compress(rot=127, st=63, sh=0, sw=0) == BS_ERR_ARG
+    assert _compress(rot=130, st=65, sh=0, sw=0) == BS_ERR_ARG
+    assert _compress(rot=64) == BS_ERR_ARG                  # sections sum to 64, not 32
+    assert _compress(st=-1, sh=41) == BS_ERR_ARG
+    assert _compress(theta=0.0) == BS_ERR_ARG
+    assert _compress(theta=float("inf")) == BS_ERR_ARG
+    assert _compress(theta=float("nan")) == BS_ERR_ARG
+    assert _compress(pt_stride=0) == BS_ERR_ARG
+    assert _compress(num_pages=0) == BS_ERR_ARG
+    for k in ("k_raw", "ptr", "start", "ring", "pt", "kc"):
+        assert _compress(**{k: NULL}) == BS_ERR_NULL, k
+    assert _compress(mpos=FAKE) == BS_ERR_NULL              # MRoPE positions need ring_pos
