@@ -173,4 +173,22 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Loads 64 lanes x 16 bytes from a buffer straight into LDS (no VGPRs): lane
+// i reads at byte `voffset` of the resource and writes LDS bytes
+// lds_addr + 16*i .. +15 (M0 holds the wave-uniform LDS address).  The
+// transfer is counted by vmcnt; the caller waits with s_waitcnt before a
+// barrier publishes the data.  Out-of-range lanes of the resource write zeros.
+__device__ __forceinline__ void lds_dma_b128(const u32x4_t& rsrc, uint32_t voffset, uint32_t lds_addr) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)rsrc.y << 32) | rsrc.x), (short)0, rsrc.z, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds_addr, 16, voffset, 0, 0, 0);
+}
+
+// vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 }  // namespace bs

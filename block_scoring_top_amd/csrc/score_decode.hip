@@ -24,15 +24,18 @@
 // product goes to the matrix cores instead (score_rows_mfma_kernel):
 //   * v_mfma_f32_16x16x32_bf16 with A = the request's query head-rows (a
 //     row's 4 heads on adjacent M rows, up to 4*NMS rows per pass), B = 16
-//     keys straight from HBM into registers in the B-fragment layout (lane
-//     l reads 16 bytes of key l%16 per k-step: the 64 lanes read the 16 keys'
-//     4 KiB once), no LDS: every wave holds all of the request's rows;
+//     keys: every wave holds all of the request's rows;
+//   * each wave copies its 16-key subtiles (4 KiB, one page) from HBM
+//     straight into LDS with 1 KiB contiguous transfers (buffer loads with the
+//     LDS flag, full cache lines), then reads its B fragments from there
+//     (swizzled, no bank conflicts).  Reading the fragments straight from HBM
+//     made 64-byte requests, and was bound by the request rate at about half
+//     the bandwidth.  Keys stay in LDS across row passes;
 //   * in the 16x16 accumulator a lane holds the 4 heads of one (row, key):
 //     ReLU, head sum and scale stay in the lane, 16 lanes store 64 contiguous
 //     bytes of a row;
 //   * a 16-key subtile lies in one page, so its page id is wave-uniform (the
-//     chunk's page ids sit one per lane and are read with v_readlane); each
-//     wave keeps P subtiles of loads in flight.
+//     chunk's page ids sit one per lane and are read with v_readlane).
 #include "device.h"
 #include "kernels.h"
 
@@ -158,13 +161,17 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   }
 }
 
-template <int NMS, int P>
-__global__ __launch_bounds__(256) void score_rows_mfma_kernel(
+template <int NMS, int NW, int KSUB>
+__global__ __launch_bounds__(64 * NW) void score_rows_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kcache, int64_t num_pages,
     const int32_t* __restrict__ page_table, int32_t pt_stride,
     const int32_t* __restrict__ req_row_ptr, const int32_t* __restrict__ row_pos,
     int32_t c, int32_t max_vis, int32_t chunk,
     float* __restrict__ scores, int64_t ld, int32_t* __restrict__ row_len) {
+  // Per wave KSUB subtiles of 16 keys (4 KiB each), key n of a subtile at
+  // bytes 256*n, its 16-byte slice s at slot s ^ n (the 16 lanes reading one
+  // k-step slice of 16 keys then hit 16 different slots: no bank conflicts).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NW][KSUB][4096];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,32 +191,20 @@ __global__ __launch_bounds__(256) void score_rows_mfma_kernel(
   const int j1 = min(j0 + chunk, nmax);
   if (j0 >= j1) return;
   const int per_page = kPage / c;
-  // The chunk spans at most 64 pages: lane i holds the chunk's i-th page id.
+  // The chunk spans at most 64 pages: lane i holds the chunk's i-th page id
+  // (chunks are at most 16*NW*KSUB <= 1,024 keys).
   const int32_t* pt = page_table + (int64_t)b * pt_stride;
   const int first_page = (c * j0) >> 6;
   const int npages = ((c * (j1 - 1)) >> 6) - first_page + 1;
   const int32_t my_page = lane < npages ? pt[first_page + lane] : -1;
   const int nsub = (j1 - j0 + 15) / 16;
 
-  // B fragment of subtile s (keys j0 + 16*s ..): lane reads key i16 (clamped
-  // to the chunk), dims 32*ks + 8*g .. +7 for ks = 0..3.  valid: the page id
-  // is in range (uniform over the subtile).
-  auto load_sub = [&](int s, u32x4_t(&br)[4], bool& valid) {
-    const int jb = j0 + 16 * s;
-    const int page = __builtin_amdgcn_readlane(my_page, ((c * jb) >> 6) - first_page);
-    valid = page >= 0 && page < num_pages;
-    const int key = min(jb + i16, j1 - 1);
-    const int64_t slot = valid ? (int64_t)page * per_page + (key & (per_page - 1)) : 0;
-    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(kcache + slot * kDim) + g;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) br[ks] = __builtin_nontemporal_load(kp + 4 * ks);
-  };
-
-  for (int g0 = r0; g0 < r1; g0 += 4 * NMS) {
-    // A fragments: subtile ms holds rows g0 + 4*ms .. +3, head-row i16 =
-    // 4*(row) + head; k-step ks covers dims 32*ks + 8*g.
-    bf16x8_t afr[NMS][4];
-    int orow[NMS], nv[NMS];
+  // A fragments of rows g0 .. g0 + 4*NMS - 1: subtile ms holds rows
+  // g0 + 4*ms .. +3, head-row i16 = 4*(row) + head; k-step ks covers dims
+  // 32*ks + 8*g.
+  bf16x8_t afr[NMS][4];
+  int orow[NMS], nv[NMS];
+  auto load_rows = [&](int g0) {
 #pragma unroll
     for (int ms = 0; ms < NMS; ++ms) {
       const int qr = g0 + 4 * ms + (i16 >> 2);
@@ -222,39 +217,71 @@ __global__ __launch_bounds__(256) void score_rows_mfma_kernel(
       orow[ms] = g0 + 4 * ms + g;  // the accumulator row this lane stores
       nv[ms] = orow[ms] < r1 ? max(0, min((row_pos[orow[ms]] + 1) / c, max_vis)) : 0;
     }
-    // This wave's subtiles: wave, wave + 4, ...; P in flight.
-    u32x4_t br[P][4];
-    bool bv[P];
+  };
+  load_rows(r0);
+
+  // This wave's subtiles s = wave + NW*p: their 16 keys lie in one page (a
+  // 16-aligned run of keys, 64/c >= 16 keys per page), copied into LDS with
+  // four 1 KiB transfers (lane l of transfer e fills slot l % 16 of key
+  // 4*e + l/16, i.e. reads that key's slice (l % 16) ^ key).  Keys past the
+  // chunk or behind an invalid page id read as zeros (buffer range check).
+  bool valid[KSUB];
+  const uint32_t lds_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(&lds[wave][0][0]);
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-      if (wave + 4 * p < nsub) load_sub(wave + 4 * p, br[p], bv[p]);
-    for (int s0 = wave; s0 < nsub; s0 += 4 * P) {
+  for (int p = 0; p < KSUB; ++p) {
+    const int s = wave + NW * p;
+    const int jb = j0 + 16 * s;
+    const int page = __builtin_amdgcn_readlane(my_page, ((c * min(jb, j1 - 1)) >> 6) - first_page);
+    valid[p] = s < nsub && page >= 0 && page < num_pages;
+    uint64_t base = reinterpret_cast<uint64_t>(kcache);
+    uint32_t bytes = 0;
+    if (valid[p]) {
+      base += (uint64_t)(((int64_t)page * per_page + (jb & (per_page - 1))) * kDim * 2);
+      bytes = (uint32_t)(min(j1 - jb, 16) * kDim * 2);
+    }
+    const u32x4_t rs = u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, 0x00020000u};
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int s = s0 + 4 * p;
-        if (s < nsub) {
-          f32x4_t acc[NMS];
-          const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int ms = 0; ms < NMS; ++ms)
-              acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], __builtin_bit_cast(bf16x8_t, br[p][ks]),
-                                                                ks == 0 ? zero : acc[ms], 0, 0, 0);
-          const bool ok = bv[p];
-          if (s + 4 * P < nsub) load_sub(s + 4 * P, br[p], bv[p]);  // refill this slot
-          const int j = j0 + 16 * s + i16;
-#pragma unroll
-          for (int ms = 0; ms < NMS; ++ms) {
-            const f32x4_t a = acc[ms];
-            const float sc = ((fmaxf(a.x, 0.f) + fmaxf(a.y, 0.f)) + (fmaxf(a.z, 0.f) + fmaxf(a.w, 0.f))) * kScale;
-            if (j < j1 && j < nv[ms]) scores[(int64_t)orow[ms] * ld + j] = ok ? sc : __builtin_nanf("");
-          }
-        }
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int n = 4 * e + (lane >> 4);
+      lds_dma_b128(rs, (uint32_t)(n * 256 + 16 * ((lane & 15) ^ n)), lds_wave + (uint32_t)(p * 4096 + e * 1024));
     }
   }
+  wait_vmcnt<0>();  // this wave's keys (and rows) are in
+
+  for (int g0 = r0;;) {
+#pragma unroll
+    for (int p = 0; p < KSUB; ++p) {
+      const int s = wave + NW * p;
+      if (s >= nsub) break;
+      const uint8_t* tile = lds[wave][p];
+      bf16x8_t br[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        br[ks] = __builtin_bit_cast(bf16x8_t,
+                                    *reinterpret_cast<const u32x4_t*>(tile + i16 * 256 + 16 * ((4 * ks + g) ^ i16)));
+      f32x4_t acc[NMS];
+      const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+          acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], br[ks], ks == 0 ? zero : acc[ms], 0, 0, 0);
+      const int j = j0 + 16 * s + i16;
+#pragma unroll
+      for (int ms = 0; ms < NMS; ++ms) {
+        const f32x4_t a = acc[ms];
+        const float sc = ((fmaxf(a.x, 0.f) + fmaxf(a.y, 0.f)) + (fmaxf(a.z, 0.f) + fmaxf(a.w, 0.f))) * kScale;
+        if (j < j1 && j < nv[ms]) scores[(int64_t)orow[ms] * ld + j] = valid[p] ? sc : __builtin_nanf("");
+      }
+    }
+    g0 += 4 * NMS;
+    if (g0 >= r1) break;
+    load_rows(g0);  // further rows reuse the keys held in LDS
+  }
 }
+
+constexpr int kRowsWaves = 4;  // waves per workgroup in the matrix-core kernel
+constexpr int kRowsSub = 2;    // 16-key subtiles per wave there
 
 static int pick_rg(int num_rows, int num_req) {
   const int avg = (num_rows + num_req - 1) / num_req;
@@ -277,19 +304,19 @@ int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_p
   dim3 grid(nchunks, num_req), block(256);
   const int rg = pick_rg(num_rows, num_req);
   if (rg >= 4) {
-    // Several rows per request: the matrix-core kernel, 256-key chunks.
-    constexpr int kChunkM = 256, P = 2;
+    // Several rows per request: the matrix-core kernel, 64*KSUB-key chunks.
+    constexpr int P = kRowsSub, W = kRowsWaves, kChunkM = 16 * W * P;
     const int nch = max_vis > 0 ? (max_vis + kChunkM - 1) / kChunkM : 1;
     const int avg = (num_rows + num_req - 1) / num_req;
     dim3 gm(nch, num_req);
     if (avg <= 4)
-      hipLaunchKernelGGL((score_rows_mfma_kernel<1, P>), gm, block, 0, stream, q, kcache, num_pages, page_table,
+      hipLaunchKernelGGL((score_rows_mfma_kernel<1, W, P>), gm, dim3(64 * W), 0, stream, q, kcache, num_pages, page_table,
                          pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
     else if (avg <= 8)
-      hipLaunchKernelGGL((score_rows_mfma_kernel<2, P>), gm, block, 0, stream, q, kcache, num_pages, page_table,
+      hipLaunchKernelGGL((score_rows_mfma_kernel<2, W, P>), gm, dim3(64 * W), 0, stream, q, kcache, num_pages, page_table,
                          pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
     else
-      hipLaunchKernelGGL((score_rows_mfma_kernel<4, P>), gm, block, 0, stream, q, kcache, num_pages, page_table,
+      hipLaunchKernelGGL((score_rows_mfma_kernel<4, W, P>), gm, dim3(64 * W), 0, stream, q, kcache, num_pages, page_table,
                          pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
     return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
   }
