@@ -66,6 +66,7 @@ constexpr int kHistChunk = 4096;               // entries per workgroup in the l
 constexpr int kHistPerLane = kHistChunk / kLongNT;
 static_assert(kHistChunk % (2 * kLongNT) == 0, "histogram chunks are whole lane pairs");
 constexpr int kChunkPages = 4 * kChunk / kPage;  // logical pages a chunk's blocks span (c <= 4)
+constexpr int kRowPages = 1024;                  // a row's first page ids, cached in LDS for its translation
 static_assert(kChunk % kLongNT == 0, "a long-row chunk is a whole number of lanes");
 
 // Workspace record per row (long rows only): merged histogram, counters
@@ -90,6 +91,8 @@ struct TopkShared {
   uint32_t base_up, base_cand;
   uint64_t red_and[16], red_or[16];
   int32_t pages[kChunkPages];  // page ids of a long-row chunk's token range (fused translation)
+  int32_t row_pages[kRowPages];  // page ids 0 .. row_npages-1 of a whole row's request (fused translation)
+  uint32_t row_npages;
 };
 
 // Translation context (fused kernels only).
@@ -311,7 +314,7 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc
     if ((uint32_t)(i * NT + tid) < nc && (key[i] & mask) >= prefix) {
       if (pos < (uint32_t)limit) {
         const int idx = index_of(key[i]);
-        out[pos] = idx;
+        if (out) out[pos] = idx;
         if (chosen) chosen[pos] = idx;
         if (wt.pt) {
           const bool valid = idx >= 0 && idx < wt.nv;
@@ -415,7 +418,7 @@ __device__ __forceinline__ void block_refine_from_row(TopkShared<CAP>& s, const 
     }
     const uint32_t pos = wave_reserve(&s.emit, p);
     if (p && pos < (uint32_t)limit) {
-      out[pos] = i;
+      if (out) out[pos] = i;
       if (chosen) chosen[pos] = i;
     }
   }
@@ -452,7 +455,7 @@ __device__ __forceinline__ void emit_tile(TopkShared<CAP>& s, float (&x)[V], int
       const uint32_t b = bin_of(x[i]);
       if (b > T) {
         if (pu < (uint32_t)m) {
-          out[pu] = idx;
+          if (out) out[pu] = idx;
           if (keep) s.chosen[pu] = idx;
         }
         ++pu;
@@ -484,9 +487,9 @@ __device__ __forceinline__ void threshold_to_shared(TopkShared<CAP>& s, uint32_t
 // the histogram (skipped when it is ready), once in NT*V-entry tiles for
 // emission.  HIST_READY: s.hist
 // already holds the row's histogram (long-row finisher).  All lanes call.
-template <int NT, int V, int CAP, bool HIST_READY, bool STREAM = true>
+template <int NT, int V, int CAP, bool HIST_READY, bool STREAM, class PF>
 __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m,
-                                           int32_t* __restrict__ out, bool keep) {
+                                           int32_t* __restrict__ out, bool keep, PF& pf) {
   constexpr int kTile = V;
   const int tid = threadIdx.x;
   if (!HIST_READY)
@@ -512,6 +515,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
     float x[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) x[i] = rd.at(tid, i * NT);  // every load in flight at once
+    pf.issue();
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       if (p % 4 == 0) __builtin_amdgcn_sched_barrier(0);  // a few bins live at a time
@@ -532,6 +536,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
       asm volatile("" : "+v"(code));  // packed here, not sunk past the loop
       pb[p] = code;
     }
+    pf.commit(s);
     __syncthreads();
     threshold_to_shared(s, (uint32_t)m);
     T = s.T;
@@ -564,7 +569,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
       upm &= upm - 1;
       if (pu < (uint32_t)m) {
         const int idx = i * NT + tid;
-        out[pu] = idx;
+        if (out) out[pu] = idx;
         if (keep) s.chosen[pu] = idx;
       }
       ++pu;
@@ -592,6 +597,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
       }
     }
   } else {
+    pf.issue();
     if (!HIST_READY) {
       for (int b0 = 0; b0 < n; b0 += NT * 8) {
         float x[8];
@@ -602,6 +608,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
           if (b0 + j * NT + tid < n) atomicAdd(&s.hist[bin_of(x[j])], 1u);
       }
     }
+    pf.commit(s);
     __syncthreads();
     threshold_to_shared(s, (uint32_t)m);
     T = s.T;
@@ -623,7 +630,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
         const uint32_t at = above + i;
         if (at < (uint32_t)m) {
           const int idx = index_of(s.cand[i]);
-          out[at] = idx;
+          if (out) out[at] = idx;
           if (keep) s.chosen[at] = idx;
         }
       }
@@ -736,28 +743,45 @@ __device__ __forceinline__ void translate_tail(const Translate& tr, const RowGeo
 // entries of a block share one address), then writes them.
 template <int NT>
 __device__ __forceinline__ void translate_row(const Translate& tr, const RowGeom& g, int r, int m,
-                                              const int32_t* chosen) {
+                                              const int32_t* chosen, const int32_t* cached = nullptr,
+                                              int ncached = 0) {
   constexpr int E = 8;
   const int c = tr.c, sh = c == 4 ? 2 : 0;
   const int nblk = c * m, total = nblk + g.p;
   const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
   int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out;
   int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out : nullptr;
+  // Every position lies at or before t: when the cache covers page t/64 (and
+  // the row's pages are in the table) no page id is read from global memory.
+  // The branch is uniform, so that path holds no global load at all: a load
+  // there, even one no lane takes, brings a wait that also waits for every
+  // store the selection issued before it.
+  const bool all_cached = g.t >= 0 && (g.t >> 6) < ncached;
   for (int i0 = 0; i0 < tr.ld_out; i0 += E * NT) {
     int pos[E], page[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = i0 + e * NT + (int)threadIdx.x;
-      int ps = -1, pg = -1;
+      int ps = -1;
       if (i < nblk) {
         const int j = chosen[i >> sh];
         if (j >= 0 && j < g.nv) ps = c * j + (i & (c - 1));
       } else if (i < total) {
         ps = c * g.nv + (i - nblk);
       }
-      if (ps >= 0 && (ps >> 6) < tr.pt_stride) pg = pt[ps >> 6];
       pos[e] = ps;
-      page[e] = pg;
+    }
+    if (all_cached) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) page[e] = pos[e] >= 0 ? cached[pos[e] >> 6] : -1;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int ps = pos[e];
+        int pg = -1;
+        if (ps >= 0 && (ps >> 6) < tr.pt_stride) pg = (ps >> 6) < ncached ? cached[ps >> 6] : pt[ps >> 6];
+        page[e] = pg;
+      }
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -771,6 +795,44 @@ __device__ __forceinline__ void translate_row(const Translate& tr, const RowGeom
   if (threadIdx.x == 0) tr.out_count[r] = total;
 }
 
+// Page ids of a row's first kRowPages logical pages, for its fused
+// translation: read right after the row's scores are issued (so their
+// latency hides behind the binning) and put in LDS before the barrier that
+// follows it.  Without them the translation waited for page-table reads that
+// also waited for the selection's stores (vector memory operations retire in
+// order).  ON = false: does nothing.
+template <int NT, bool ON>
+struct RowPagePrefetch {
+  static constexpr int PER = (kRowPages + NT - 1) / NT;
+  const Translate& tr;
+  int r;
+  RowGeomReads gr;
+  RowGeom g{};
+  int np = 0;
+  int32_t v[PER];
+  __device__ __forceinline__ void issue() {
+    if (!ON) return;
+    g = row_geometry_finish(tr, r, gr);
+    np = g.t >= 0 ? min((g.t >> 6) + 1, min(kRowPages, tr.pt_stride)) : 0;
+    const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = i * NT + (int)threadIdx.x;
+      v[i] = idx < np ? pt[idx] : -1;
+    }
+  }
+  template <int CAP>
+  __device__ __forceinline__ void commit(TopkShared<CAP>& s) {
+    if (!ON) return;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = i * NT + (int)threadIdx.x;
+      if (idx < kRowPages) s.row_pages[idx] = v[i];
+    }
+    if (threadIdx.x == 0) s.row_npages = (uint32_t)np;
+  }
+};
+
 // The whole selection of one row by one workgroup, any n.
 template <int NT, int VPT, int CAP, bool TRANSLATE, bool STREAM = true>
 __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m, int k,
@@ -779,20 +841,21 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float
   const int tid = threadIdx.x;
   RowGeomReads gr{};
   if (TRANSLATE) gr = row_geometry_start(tr, r);  // in flight during the selection
-  for (int i = m + tid; i < k; i += NT) out[i] = -1;
-  if (tid == 0) sel_count[r] = m;
+  RowPagePrefetch<NT, TRANSLATE> pf{tr, r, gr};
+  // The selection is staged in LDS and written out once it is complete: a
+  // global store issued early would hold up every later wait for a load
+  // (vector memory operations retire in order).
   if (m == n) {
-    for (int i = tid; i < n; i += NT) {
-      out[i] = i;
-      if (TRANSLATE) s.chosen[i] = i;
-    }
+    pf.issue();
+    for (int i = tid; i < n; i += NT) s.chosen[i] = i;
+    pf.commit(s);
   } else {
-    select_row<NT, VPT, CAP, false, STREAM>(s, row, n, m, out, TRANSLATE);
+    select_row<NT, VPT, CAP, false, STREAM>(s, row, n, m, nullptr, true, pf);
   }
-  if (TRANSLATE) {
-    __syncthreads();
-    translate_row<NT>(tr, row_geometry_finish(tr, r, gr), r, m, s.chosen);
-  }
+  __syncthreads();
+  for (int i = tid; i < k; i += NT) out[i] = i < m ? s.chosen[i] : -1;
+  if (tid == 0) sel_count[r] = m;
+  if (TRANSLATE) translate_row<NT>(tr, pf.g, r, m, s.chosen, s.row_pages, (int)s.row_npages);
 }
 
 // One workgroup of NT lanes per row.  Three shapes: 1,024 lanes holding 16
