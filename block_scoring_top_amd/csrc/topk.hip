@@ -740,23 +740,20 @@ __device__ __forceinline__ void translate_tail(const Translate& tr, const RowGeo
 // covers 256 contiguous bytes; entry i < c*m belongs to selection position
 // i / c (c is 1 or 4), entries from c*m on are the pending tail, then -1.
 // Each round reads the page ids of its E entries per lane first (the c
-// entries of a block share one address), then writes them.
-template <int NT>
-__device__ __forceinline__ void translate_row(const Translate& tr, const RowGeom& g, int r, int m,
-                                              const int32_t* chosen, const int32_t* cached = nullptr,
-                                              int ncached = 0) {
+// entries of a block share one address), then writes them.  CACHED: every
+// page id comes from `cached` (LDS).  That path holds no global load at
+// all: a load there, even one no lane takes, brings a wait that also waits
+// for every store issued before it (vector memory operations retire in
+// order), so the two cases are separate code down to the stores.
+template <int NT, bool CACHED>
+__device__ __forceinline__ void translate_rounds(const Translate& tr, const RowGeom& g, int r, int m,
+                                                 const int32_t* chosen, const int32_t* cached, int ncached) {
   constexpr int E = 8;
   const int c = tr.c, sh = c == 4 ? 2 : 0;
   const int nblk = c * m, total = nblk + g.p;
   const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
   int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out;
   int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out : nullptr;
-  // Every position lies at or before t: when the cache covers page t/64 (and
-  // the row's pages are in the table) no page id is read from global memory.
-  // The branch is uniform, so that path holds no global load at all: a load
-  // there, even one no lane takes, brings a wait that also waits for every
-  // store the selection issued before it.
-  const bool all_cached = g.t >= 0 && (g.t >> 6) < ncached;
   for (int i0 = 0; i0 < tr.ld_out; i0 += E * NT) {
     int pos[E], page[E];
 #pragma unroll
@@ -769,19 +766,14 @@ __device__ __forceinline__ void translate_row(const Translate& tr, const RowGeom
       } else if (i < total) {
         ps = c * g.nv + (i - nblk);
       }
-      pos[e] = ps;
-    }
-    if (all_cached) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) page[e] = pos[e] >= 0 ? cached[pos[e] >> 6] : -1;
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int ps = pos[e];
-        int pg = -1;
-        if (ps >= 0 && (ps >> 6) < tr.pt_stride) pg = (ps >> 6) < ncached ? cached[ps >> 6] : pt[ps >> 6];
-        page[e] = pg;
+      int pg = -1;
+      if (CACHED) {
+        if (ps >= 0) pg = cached[ps >> 6];
+      } else if (ps >= 0 && (ps >> 6) < tr.pt_stride) {
+        pg = (ps >> 6) < ncached ? cached[ps >> 6] : pt[ps >> 6];
       }
+      pos[e] = ps;
+      page[e] = pg;
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -793,6 +785,19 @@ __device__ __forceinline__ void translate_row(const Translate& tr, const RowGeom
     }
   }
   if (threadIdx.x == 0) tr.out_count[r] = total;
+}
+
+// Every position of the row lies at or before t, so when the cache holds
+// page t/64 (which implies t/64 < pt_stride) no page id is read from global
+// memory.  The branch is uniform.
+template <int NT>
+__device__ __forceinline__ void translate_row(const Translate& tr, const RowGeom& g, int r, int m,
+                                              const int32_t* chosen, const int32_t* cached = nullptr,
+                                              int ncached = 0) {
+  if (g.t >= 0 && (g.t >> 6) < ncached)
+    translate_rounds<NT, true>(tr, g, r, m, chosen, cached, ncached);
+  else
+    translate_rounds<NT, false>(tr, g, r, m, chosen, cached, ncached);
 }
 
 // Page ids of a row's first kRowPages logical pages, for its fused
