@@ -219,6 +219,94 @@ def test_expand_exact_on_oracle_selection(c):
     check_expand_exact(slots, pos, oc, ref["slots"], ref["pos"], ref["out_count"], gu.pending_counts(inp))
 
 
+def _many_rows_batch(rng, n_req, rows_per_req, c, k, long_ctx=200_000, n_long=6):
+    """A batch of many rows for the expansion alone (no keys are read): most
+    requests hold 2-9K tokens, n_long of them long_ctx tokens (more than the
+    2,048 pages the row kernel caches), pages a seeded permutation."""
+    ctx = [int(x) for x in rng.integers(2000, 9000, n_req)]
+    for i in rng.choice(n_req, n_long, replace=False):
+        ctx[i] = long_ctx
+    pages = [-(-t // 64) for t in ctx]
+    perm = rng.permutation(int(sum(pages)))
+    pt = np.full((n_req, max(pages)), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        pt[b, :n] = perm[off:off + n]
+        off += n
+    rows = [ctx[b] - 1 - np.sort(rng.choice(min(ctx[b], 500), rows_per_req, replace=False))[::-1]
+            for b in range(n_req)]
+    row_pos = np.concatenate(rows).astype(np.int32)
+    ptr = np.arange(0, n_req * rows_per_req + 1, rows_per_req, dtype=np.int32)
+    per_page = 64 // c
+    return synth.IndexerInputs(name="many", c=c, k=k, q=np.zeros((row_pos.shape[0], 4, 128), np.uint16),
+                               kcache=np.zeros((per_page, 128), np.uint16), num_pages=int(off),
+                               page_table=pt, req_row_ptr=ptr, row_pos=row_pos,
+                               max_vis=int(((row_pos.astype(np.int64) + 1) // c).max()), seed=0)
+
+
+def _random_selection(rng, inp):
+    """min(k, n_vis) distinct visible blocks per row, in random order."""
+    R = inp.num_rows
+    sel = np.full((R, inp.k), -1, dtype=np.int32)
+    cnt = np.zeros(R, dtype=np.int32)
+    for r in range(R):
+        nv = (int(inp.row_pos[r]) + 1) // inp.c
+        m = min(inp.k, nv)
+        sel[r, :m] = rng.choice(nv, m, replace=False)
+        cnt[r] = m
+    return sel, cnt
+
+
+@pytest.mark.parametrize("c", [1, 4])
+def test_expand_many_rows_exact(c):
+    # >= 1,024 rows: the one-workgroup-per-row expansion, including rows whose
+    # pages exceed its LDS page cache
+    rng = np.random.default_rng(80 + c)
+    inp = _many_rows_batch(rng, 180, 6, c, 512 if c == 4 else 2048)
+    assert inp.num_rows >= 1024 and int(inp.row_pos.max()) // 64 >= 2048
+    sel, cnt = _random_selection(rng, inp)
+    rs, rp, rc = oracle.expand_translate(inp, sel, cnt)
+    slots, pos, oc = gu.gpu_expand(inp, sel, cnt)
+    check_expand_exact(slots, pos, oc, rs, rp, rc, gu.pending_counts(inp))
+
+
+def test_expand_shared_many_rows_exact():
+    rng = np.random.default_rng(90)
+    N = 5
+    inp = _many_rows_batch(rng, 180, 6, 4, 512)
+    sel, cnt = _random_selection(rng, inp)
+    now = inp.row_pos + rng.integers(0, N + 1, inp.num_rows).astype(np.int32)
+    rs, rp, rc = oracle.expand_translate_shared(inp, sel, cnt, now, N)
+    slots, pos, oc = gu.gpu_expand_shared(inp, sel, cnt, now, N)
+    tail = now + 1 - 4 * ((inp.row_pos + 1) // 4)
+    check_expand_exact(slots, pos, oc, rs, rp, rc, tail)
+
+
+def test_expand_many_rows_invalid_entries_become_sentinels():
+    rng = np.random.default_rng(91)
+    inp = _many_rows_batch(rng, 180, 6, 4, 512, n_long=2)
+    sel, cnt = _random_selection(rng, inp)
+    bad = rng.random(sel.shape) < 0.01
+    live = np.arange(inp.k)[None, :] < cnt[:, None]
+    nv = (inp.row_pos.astype(np.int64) + 1) // 4
+    sel[bad & live] = np.where(rng.random(int((bad & live).sum())) < 0.5, -1,
+                               np.repeat(nv, inp.k).reshape(sel.shape)[bad & live])
+    slots, pos, oc = gu.gpu_expand(inp, sel, cnt)
+    assert np.array_equal(oc, 4 * cnt + gu.pending_counts(inp))
+    R, k = sel.shape
+    live = np.arange(k)[None, :] < cnt[:, None]
+    ok = live & (sel >= 0) & (sel < nv[:, None])
+    assert (live & ~ok).sum() > 100
+    b = np.searchsorted(inp.req_row_ptr, np.arange(R), side="right") - 1
+    want_pos = np.where(ok[..., None], 4 * sel[..., None] + np.arange(4), -1)
+    page = inp.page_table[b[:, None], np.clip(4 * sel // 64, 0, inp.pt_stride - 1)]
+    want_slot = np.where(ok[..., None], page[..., None] * 64 + want_pos % 64, -1)
+    got_pos = pos[:, :4 * k].reshape(R, k, 4)
+    got_slot = slots[:, :4 * k].reshape(R, k, 4)
+    assert np.array_equal(got_pos[live], want_pos[live])
+    assert np.array_equal(got_slot[live], want_slot[live])
+
+
 def test_expand_invalid_entries_become_sentinels():
     inp = synth.qsa_decode_1x8k()
     sel = np.full((1, inp.k), -1, dtype=np.int32)
