@@ -162,6 +162,23 @@ def test_topk_mixed_lengths_one_launch():
         check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
 
 
+@pytest.mark.parametrize("R", [256, 257])
+def test_topk_long_row_count_boundary(R):
+    # Up to 256 rows of >= 32,769 entries split each row over many workgroups
+    # (workspace, device atomics); one more row and every row streams through
+    # one workgroup.  Odd k values, ragged lengths, tie storms.
+    n = 33000
+    rng = np.random.default_rng(R)
+    rows = rng.standard_normal((R, n)).astype(np.float32)
+    rows[:16] = synth.tie_storm_rows(R + 5, 16, n)
+    lens = rng.integers(32769, n + 1, R).astype(np.int32)
+    lens[-4:] = [0, 1, 2048, 32768]
+    for k in (3, 1000, 2047):
+        (out,), _ = gu.gpu_topk(rows, lens, k)
+        ref_sel, ref_cnt = oracle.topk(rows, lens, k)
+        check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
+
+
 def test_topk_overflowing_boundary_bin():
     # more than 4,096 entries tie in the boundary bin: exercises the re-scan refinement
     rng = np.random.default_rng(8)
