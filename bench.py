@@ -313,7 +313,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): every call of this path runs on one "
-              "GPU with no collectives; see the sharding note in DESIGN.md", file=sys.stderr)
+              "GPU with no collectives, and no multi-GPU form is built", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,6 +1,6 @@
 """Builds the CPU oracle (plain C, OpenMP) into ``oracle/liboracle.so``.
 
-Test infrastructure only: the oracle is the checker, never part of the product.
+Test infrastructure only: the tests compare the HIP path with it; it is never part of the product.
 """
 from __future__ import annotations
 

@@ -22,8 +22,8 @@ def _gpu_available() -> bool:
 
 
 def pytest_collection_modifyitems(config, items):
-    # Tests marked gpu are skipped only when no GPU is visible at all (the CPU
-    # container).  On a GPU machine a missing HIP library is an error, not a skip.
+    # Tests marked gpu are skipped only when no GPU is visible at all.  Where a
+    # GPU is visible, a missing HIP library is an error, not a skip.
     if _gpu_available():
         return
     skip = pytest.mark.skip(reason="no GPU visible")
