@@ -27,7 +27,11 @@ CFLAGS = [
 # Per-source extras.  The prefill scorer keeps its MFMA accumulators in
 # architectural VGPRs (gfx950 allows either file): its epilogue then reads them
 # without v_accvgpr moves, at the same occupancy.
-EXTRA = {"score_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The top-k kernels issue their device atomics from one lane and use the
+# result later: the atomic optimizer's wave-level rewrite reads the result at
+# once (a wait on every atomic), so it is turned off there.
+EXTRA = {"score_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "topk.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str, objdir: str, verbose: bool) -> str:

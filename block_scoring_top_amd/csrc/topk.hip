@@ -1035,11 +1035,12 @@ __global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
   }
   uint32_t total;
   const uint32_t excl = block_excl_scan<kLongNT>(s, (nup << 20) | neq, total);
+  // The list offsets are reserved first and published after the staging
+  // below, so the atomics' round trip overlaps it.
+  uint32_t bu, bc;  // read by lane 0 only
   if (tid == 0) {
-    s.base_up = (total >> 20) ? __hip_atomic_fetch_add(&ctr[1], total >> 20, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT) : 0u;
-    s.base_cand = (total & 0xFFFFFu) ? __hip_atomic_fetch_add(&ctr[2], total & 0xFFFFFu, __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    bu = __hip_atomic_fetch_add(&ctr[1], total >> 20, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bc = __hip_atomic_fetch_add(&ctr[2], total & 0xFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // Stage this workgroup's picks in LDS at their scanned offsets (the
   // running per-lane counters keep each lane's picks in index order), then
@@ -1058,6 +1059,10 @@ __global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
         ++le;
       }
     }
+  }
+  if (tid == 0) {
+    s.base_up = bu;
+    s.base_cand = bc;
   }
   __syncthreads();
   const uint32_t tot_up = min(total >> 20, (uint32_t)kKmax), tot_eq = min(total & 0xFFFFFu, (uint32_t)kLongCand);
