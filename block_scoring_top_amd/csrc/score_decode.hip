@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64 * NW) void score_rows_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kcache, int64_t num_pages,
     const int32_t* __restrict__ page_table, int32_t pt_stride,
     const int32_t* __restrict__ req_row_ptr, const int32_t* __restrict__ row_pos,
-    int32_t c, int32_t max_vis, int32_t chunk,
+    int32_t c, int32_t max_vis, int32_t chunk, int32_t fold,
     float* __restrict__ scores, int64_t ld, int32_t* __restrict__ row_len) {
   // Per wave KSUB subtiles of 16 keys (4 KiB each), key n of a subtile at
   // bytes 256*n, its 16-byte slice s at slot s ^ n (the 16 lanes reading one
@@ -187,96 +187,100 @@ __global__ __launch_bounds__(64 * NW) void score_rows_mfma_kernel(
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off));
   nmax = __builtin_amdgcn_readfirstlane(nmax);
-  const int j0 = blockIdx.x * chunk;
-  const int j1 = min(j0 + chunk, nmax);
-  if (j0 >= j1) return;
-  const int per_page = kPage / c;
-  // The chunk spans at most 64 pages: lane i holds the chunk's i-th page id
-  // (chunks are at most 16*NW*KSUB <= 1,024 keys).
-  const int32_t* pt = page_table + (int64_t)b * pt_stride;
-  const int first_page = (c * j0) >> 6;
-  const int npages = ((c * (j1 - 1)) >> 6) - first_page + 1;
-  const int32_t my_page = lane < npages ? pt[first_page + lane] : -1;
-  const int nsub = (j1 - j0 + 15) / 16;
+  // `fold` consecutive chunks per workgroup, one after the other (each
+  // wave's LDS tiles are its own, so reusing them needs no barrier).
+  for (int f = 0; f < fold; ++f) {
+    const int j0 = (blockIdx.x * fold + f) * chunk;
+    const int j1 = min(j0 + chunk, nmax);
+    if (j0 >= j1) return;
+    const int per_page = kPage / c;
+    // The chunk spans at most 64 pages: lane i holds the chunk's i-th page id
+    // (chunks are at most 16*NW*KSUB <= 1,024 keys).
+    const int32_t* pt = page_table + (int64_t)b * pt_stride;
+    const int first_page = (c * j0) >> 6;
+    const int npages = ((c * (j1 - 1)) >> 6) - first_page + 1;
+    const int32_t my_page = lane < npages ? pt[first_page + lane] : -1;
+    const int nsub = (j1 - j0 + 15) / 16;
 
-  // A fragments of rows g0 .. g0 + 4*NMS - 1: subtile ms holds rows
-  // g0 + 4*ms .. +3, head-row i16 = 4*(row) + head; k-step ks covers dims
-  // 32*ks + 8*g.
-  bf16x8_t afr[NMS][4];
-  int orow[NMS], nv[NMS];
-  auto load_rows = [&](int g0) {
-#pragma unroll
-    for (int ms = 0; ms < NMS; ++ms) {
-      const int qr = g0 + 4 * ms + (i16 >> 2);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (qr < r1) v = *(reinterpret_cast<const u32x4_t*>(q + ((int64_t)qr * kHeads + (i16 & 3)) * kDim + 32 * ks) + g);
-        afr[ms][ks] = __builtin_bit_cast(bf16x8_t, v);
+    // A fragments of rows g0 .. g0 + 4*NMS - 1: subtile ms holds rows
+    // g0 + 4*ms .. +3, head-row i16 = 4*(row) + head; k-step ks covers dims
+    // 32*ks + 8*g.
+    bf16x8_t afr[NMS][4];
+    int orow[NMS], nv[NMS];
+    auto load_rows = [&](int g0) {
+  #pragma unroll
+      for (int ms = 0; ms < NMS; ++ms) {
+        const int qr = g0 + 4 * ms + (i16 >> 2);
+  #pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+          if (qr < r1) v = *(reinterpret_cast<const u32x4_t*>(q + ((int64_t)qr * kHeads + (i16 & 3)) * kDim + 32 * ks) + g);
+          afr[ms][ks] = __builtin_bit_cast(bf16x8_t, v);
+        }
+        orow[ms] = g0 + 4 * ms + g;  // the accumulator row this lane stores
+        nv[ms] = orow[ms] < r1 ? max(0, min((row_pos[orow[ms]] + 1) / c, max_vis)) : 0;
       }
-      orow[ms] = g0 + 4 * ms + g;  // the accumulator row this lane stores
-      nv[ms] = orow[ms] < r1 ? max(0, min((row_pos[orow[ms]] + 1) / c, max_vis)) : 0;
-    }
-  };
-  load_rows(r0);
+    };
+    load_rows(r0);
 
-  // This wave's subtiles s = wave + NW*p: their 16 keys lie in one page (a
-  // 16-aligned run of keys, 64/c >= 16 keys per page), copied into LDS with
-  // four 1 KiB transfers (lane l of transfer e fills slot l % 16 of key
-  // 4*e + l/16, i.e. reads that key's slice (l % 16) ^ key).  Keys past the
-  // chunk or behind an invalid page id read as zeros (buffer range check).
-  bool valid[KSUB];
-  const uint32_t lds_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(&lds[wave][0][0]);
-#pragma unroll
-  for (int p = 0; p < KSUB; ++p) {
-    const int s = wave + NW * p;
-    const int jb = j0 + 16 * s;
-    const int page = __builtin_amdgcn_readlane(my_page, ((c * min(jb, j1 - 1)) >> 6) - first_page);
-    valid[p] = s < nsub && page >= 0 && page < num_pages;
-    uint64_t base = reinterpret_cast<uint64_t>(kcache);
-    uint32_t bytes = 0;
-    if (valid[p]) {
-      base += (uint64_t)(((int64_t)page * per_page + (jb & (per_page - 1))) * kDim * 2);
-      bytes = (uint32_t)(min(j1 - jb, 16) * kDim * 2);
-    }
-    const u32x4_t rs = u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, 0x00020000u};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int n = 4 * e + (lane >> 4);
-      lds_dma_b128(rs, (uint32_t)(n * 256 + 16 * ((lane & 15) ^ n)), lds_wave + (uint32_t)(p * 4096 + e * 1024));
-    }
-  }
-  wait_vmcnt<0>();  // this wave's keys (and rows) are in
-
-  for (int g0 = r0;;) {
-#pragma unroll
+    // This wave's subtiles s = wave + NW*p: their 16 keys lie in one page (a
+    // 16-aligned run of keys, 64/c >= 16 keys per page), copied into LDS with
+    // four 1 KiB transfers (lane l of transfer e fills slot l % 16 of key
+    // 4*e + l/16, i.e. reads that key's slice (l % 16) ^ key).  Keys past the
+    // chunk or behind an invalid page id read as zeros (buffer range check).
+    bool valid[KSUB];
+    const uint32_t lds_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(&lds[wave][0][0]);
+  #pragma unroll
     for (int p = 0; p < KSUB; ++p) {
       const int s = wave + NW * p;
-      if (s >= nsub) break;
-      const uint8_t* tile = lds[wave][p];
-      bf16x8_t br[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        br[ks] = __builtin_bit_cast(bf16x8_t,
-                                    *reinterpret_cast<const u32x4_t*>(tile + i16 * 256 + 16 * ((4 * ks + g) ^ i16)));
-      f32x4_t acc[NMS];
-      const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int ms = 0; ms < NMS; ++ms)
-          acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], br[ks], ks == 0 ? zero : acc[ms], 0, 0, 0);
-      const int j = j0 + 16 * s + i16;
-#pragma unroll
-      for (int ms = 0; ms < NMS; ++ms) {
-        const f32x4_t a = acc[ms];
-        const float sc = ((fmaxf(a.x, 0.f) + fmaxf(a.y, 0.f)) + (fmaxf(a.z, 0.f) + fmaxf(a.w, 0.f))) * kScale;
-        if (j < j1 && j < nv[ms]) scores[(int64_t)orow[ms] * ld + j] = valid[p] ? sc : __builtin_nanf("");
+      const int jb = j0 + 16 * s;
+      const int page = __builtin_amdgcn_readlane(my_page, ((c * min(jb, j1 - 1)) >> 6) - first_page);
+      valid[p] = s < nsub && page >= 0 && page < num_pages;
+      uint64_t base = reinterpret_cast<uint64_t>(kcache);
+      uint32_t bytes = 0;
+      if (valid[p]) {
+        base += (uint64_t)(((int64_t)page * per_page + (jb & (per_page - 1))) * kDim * 2);
+        bytes = (uint32_t)(min(j1 - jb, 16) * kDim * 2);
+      }
+      const u32x4_t rs = u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, 0x00020000u};
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = 4 * e + (lane >> 4);
+        lds_dma_b128(rs, (uint32_t)(n * 256 + 16 * ((lane & 15) ^ n)), lds_wave + (uint32_t)(p * 4096 + e * 1024));
       }
     }
-    g0 += 4 * NMS;
-    if (g0 >= r1) break;
-    load_rows(g0);  // further rows reuse the keys held in LDS
+    wait_vmcnt<0>();  // this wave's keys (and rows) are in
+
+    for (int g0 = r0;;) {
+  #pragma unroll
+      for (int p = 0; p < KSUB; ++p) {
+        const int s = wave + NW * p;
+        if (s >= nsub) break;
+        const uint8_t* tile = lds[wave][p];
+        bf16x8_t br[4];
+  #pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          br[ks] = __builtin_bit_cast(bf16x8_t,
+                                      *reinterpret_cast<const u32x4_t*>(tile + i16 * 256 + 16 * ((4 * ks + g) ^ i16)));
+        f32x4_t acc[NMS];
+        const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+  #pragma unroll
+          for (int ms = 0; ms < NMS; ++ms)
+            acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ms][ks], br[ks], ks == 0 ? zero : acc[ms], 0, 0, 0);
+        const int j = j0 + 16 * s + i16;
+  #pragma unroll
+        for (int ms = 0; ms < NMS; ++ms) {
+          const f32x4_t a = acc[ms];
+          const float sc = ((fmaxf(a.x, 0.f) + fmaxf(a.y, 0.f)) + (fmaxf(a.z, 0.f) + fmaxf(a.w, 0.f))) * kScale;
+          if (j < j1 && j < nv[ms]) scores[(int64_t)orow[ms] * ld + j] = valid[p] ? sc : __builtin_nanf("");
+        }
+      }
+      g0 += 4 * NMS;
+      if (g0 >= r1) break;
+      load_rows(g0);  // further rows reuse the keys held in LDS
+    }
   }
 }
 
@@ -306,18 +310,23 @@ int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_p
   if (rg >= 4) {
     // Several rows per request: the matrix-core kernel, 64*KSUB-key chunks.
     constexpr int P = kRowsSub, W = kRowsWaves, kChunkM = 16 * W * P;
-    const int nch = max_vis > 0 ? (max_vis + kChunkM - 1) / kChunkM : 1;
+    // Two chunks per workgroup: with ragged requests most workgroups of the
+    // (chunk, request) grid find no keys, and halving their number measured
+    // 37.3 -> 35.2 us on 64 requests x 6 rows of 1,022-32,768 blocks (four
+    // chunks: 36.7 us).
+    constexpr int kFold = 2;
+    const int nch = max_vis > 0 ? ((max_vis + kChunkM - 1) / kChunkM + kFold - 1) / kFold : 1;
     const int avg = (num_rows + num_req - 1) / num_req;
     dim3 gm(nch, num_req);
     if (avg <= 4)
       hipLaunchKernelGGL((score_rows_mfma_kernel<1, W, P>), gm, dim3(64 * W), 0, stream, q, kcache, num_pages, page_table,
-                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
+                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, kFold, scores, ld, row_len);
     else if (avg <= 8)
       hipLaunchKernelGGL((score_rows_mfma_kernel<2, W, P>), gm, dim3(64 * W), 0, stream, q, kcache, num_pages, page_table,
-                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
+                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, kFold, scores, ld, row_len);
     else
       hipLaunchKernelGGL((score_rows_mfma_kernel<4, W, P>), gm, dim3(64 * W), 0, stream, q, kcache, num_pages, page_table,
-                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, scores, ld, row_len);
+                         pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, kFold, scores, ld, row_len);
     return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
   }
 #define BS_LAUNCH_DECODE(RGV)                                                                 \
