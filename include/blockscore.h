@@ -43,8 +43,10 @@
  *     kernels clamp every index so that a violation never reads or writes
  *     outside the buffers described by the host-side sizes, but the values
  *     produced for violating rows are then unspecified.
- *   - There is no global state: calls are thread-safe.  Calls that share a
- *     workspace must not overlap in time (use one stream).
+ *   - Calls are thread-safe.  The only library-wide state is the prefill
+ *     scorer's resident-workgroups-per-CU figure, computed on first use and
+ *     kept in an atomic.  Calls that share a workspace must not overlap in
+ *     time (use one stream).
  *
  * Shapes and layouts:
  *   - bf16 values travel as their uint16 bit patterns.
