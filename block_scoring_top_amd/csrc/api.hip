@@ -37,6 +37,9 @@ BS_EXPORT int idx_score_decode(const uint16_t* q, const uint16_t* kcache, int64_
                                   num_rows, c, max_vis, scores, ld_scores);
   if (st != BS_OK || num_rows == 0 || num_req == 0) return st;
   if (num_req > 65535) return BS_ERR_ARG;  // one grid row per request
+  // a row's scores are addressed through a buffer of 32-bit byte range; the
+  // same bound as the selection's rows
+  if ((int64_t)max_vis > (int64_t)65535 * 4096) return BS_ERR_ARG;
   return bs::launch_score_decode(q, kcache, num_pages, page_table, pt_stride, req_row_ptr, num_req, row_pos,
                                  num_rows, c, max_vis, scores, ld_scores, row_len,
                                  static_cast<hipStream_t>(stream));

@@ -152,8 +152,14 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
           if (i < ng) {
             const float sc = row_head_relu_sum(slice_dot(cur[u], qv[i][0]), slice_dot(cur[u], qv[i][1]),
                                                slice_dot(cur[u], qv[i][2]), slice_dot(cur[u], qv[i][3]), sub);
-            if (sub == 0 && j < j1 && j < nvis[i])
-              scores[(int64_t)(g0 + i) * ld + j] = cok[u] ? sc * kScale : __builtin_nanf("");
+            // j < j0 + chunk always holds here, so j < nvis[i] (the range
+            // of the row's buffer) is the whole store condition; lanes other
+            // than the key's first fall outside the range too.  No branch:
+            // the wait for the next keys then leaves these stores in flight.
+            const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+                scores + (int64_t)(g0 + i) * ld, (short)0, nvis[i] * 4, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cok[u] ? sc * kScale : __builtin_nanf("")), srs,
+                                                  sub == 0 ? (uint32_t)j * 4u : 0x80000000u, 0, 0);
           }
         }
       }

@@ -115,7 +115,8 @@ enum bs_status {
  * Returns BS_OK, BS_ERR_NULL (q, kcache, page_table, req_row_ptr, row_pos or
  * scores NULL with num_rows > 0), BS_ERR_ARG (c not 1 or 4, negative counts,
  * pt_stride < 1, num_pages < 1, max_vis < 0, ld_scores < max_vis,
- * c*max_vis > 64*pt_stride, num_req > 65535) or BS_ERR_LAUNCH.
+ * c*max_vis > 64*pt_stride, num_req > 65535; idx_score_decode also
+ * max_vis > 65535*4096, the selection's bound on a row) or BS_ERR_LAUNCH.
  */
 int idx_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_pages,
                      const int32_t* page_table, int32_t pt_stride,

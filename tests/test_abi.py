@@ -78,6 +78,13 @@ def test_score_validation(fn):
         assert _score(fn, **{k: NULL}) == BS_ERR_NULL, k
 
 
+def test_score_decode_row_bound():
+    # rows beyond 65,535 * 4,096 blocks are refused before any launch (every
+    # other argument valid for that size)
+    big = 65535 * 4096 + 1
+    assert _score("idx_score_decode", c=1, max_vis=big, ld=big, pt_stride=(big + 63) // 64) == BS_ERR_ARG
+
+
 def _topk(**kw):
     a = dict(scores=FAKE, ld=100000, row_len=FAKE, num_rows=2, max_len=100000, k=2048, sel=FAKE, cnt=FAKE,
              ws=FAKE, ws_bytes=1 << 30, stream=NULL)
