@@ -348,8 +348,9 @@ def prepare_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, 
 __all__ = [
     "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
     "topk_select_rows", "idx_expand_translate", "idx_expand_translate_shared", "idx_select_translate",
-    "status_string", "BlockScoreError",
+    "idx_compress_store", "status_string", "BlockScoreError",
     "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate", "prepare_expand_shared",
+    "prepare_compress_store",
 ]
 
 

@@ -21,7 +21,6 @@ inline int check_score_args(const uint16_t* q, const uint16_t* kcache, int64_t n
   if (!q || !kcache || !page_table || !req_row_ptr || !row_pos || !scores) return BS_ERR_NULL;
   if (pt_stride < 1 || num_pages < 1 || ld_scores < (int64_t)max_vis) return BS_ERR_ARG;
   if ((int64_t)c * max_vis > (int64_t)BS_PAGE_TOKENS * pt_stride) return BS_ERR_ARG;
-  if (num_req > 0x7FFFFFFF - 1) return BS_ERR_ARG;
   return BS_OK;
 }
 

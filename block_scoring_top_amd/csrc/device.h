@@ -147,6 +147,11 @@ __device__ __forceinline__ uint32_t pk_gt_flags(uint32_t codes, uint32_t t) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Blocks visible to a query row at position t (it sees tokens 0..t): those
+// whose c tokens all lie at or before t, floor((t+1)/c), capped at the
+// caller's bound max_vis and at 0 for an invalid position.
+__device__ __forceinline__ int visible_blocks(int t, int c, int max_vis) { return max(0, min((t + 1) / c, max_vis)); }
+
 // Reads FP32 entries of one row through a raw buffer resource: one lane
 // offset per load (no 64-bit address registers), and the hardware range check
 // returns 0 for entries at or past n, so reads past the row never fault.

@@ -83,10 +83,9 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
 
   int nmax = 0;
-  for (int r = r0; r < r1; ++r) nmax = max(nmax, (row_pos[r] + 1) / c);
-  nmax = min(nmax, max_vis);
+  for (int r = r0; r < r1; ++r) nmax = max(nmax, visible_blocks(row_pos[r], c, max_vis));
   if (blockIdx.x == 0 && row_len != nullptr)
-    for (int r = r0 + tid; r < r1; r += blockDim.x) row_len[r] = max(0, min((row_pos[r] + 1) / c, max_vis));
+    for (int r = r0 + tid; r < r1; r += blockDim.x) row_len[r] = visible_blocks(row_pos[r], c, max_vis);
 
   const int j0 = blockIdx.x * chunk;
   if (j0 >= nmax) return;
@@ -122,7 +121,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(
       const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(q + (int64_t)r * kHeads * kDim) + sub;
 #pragma unroll
       for (int h = 0; h < kHeads; ++h) qv[i][h] = qp[h * (kDim / 8)];
-      nvis[i] = i < ng ? min((row_pos[r] + 1) / c, max_vis) : 0;
+      nvis[i] = i < ng ? visible_blocks(row_pos[r], c, max_vis) : 0;
     }
 
     u32x4_t kv[U];
@@ -185,11 +184,11 @@ __global__ __launch_bounds__(64 * NW) void score_rows_mfma_kernel(
   const int r0 = req_row_ptr[b];
   const int r1 = req_row_ptr[b + 1];
   if (blockIdx.x == 0 && row_len != nullptr)
-    for (int r = r0 + tid; r < r1; r += blockDim.x) row_len[r] = max(0, min((row_pos[r] + 1) / c, max_vis));
+    for (int r = r0 + tid; r < r1; r += blockDim.x) row_len[r] = visible_blocks(row_pos[r], c, max_vis);
 
   // The request's longest visible range bounds the chunk.
   int nmax = 0;
-  for (int r = r0 + lane; r < r1; r += 64) nmax = max(nmax, min((row_pos[r] + 1) / c, max_vis));
+  for (int r = r0 + lane; r < r1; r += 64) nmax = max(nmax, visible_blocks(row_pos[r], c, max_vis));
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off));
   nmax = __builtin_amdgcn_readfirstlane(nmax);
@@ -224,7 +223,7 @@ __global__ __launch_bounds__(64 * NW) void score_rows_mfma_kernel(
           afr[ms][ks] = __builtin_bit_cast(bf16x8_t, v);
         }
         orow[ms] = g0 + 4 * ms + g;  // the accumulator row this lane stores
-        nv[ms] = orow[ms] < r1 ? max(0, min((row_pos[orow[ms]] + 1) / c, max_vis)) : 0;
+        nv[ms] = orow[ms] < r1 ? visible_blocks(row_pos[orow[ms]], c, max_vis) : 0;
       }
     };
     load_rows(r0);
@@ -293,10 +292,9 @@ __global__ __launch_bounds__(64 * NW) void score_rows_mfma_kernel(
 constexpr int kRowsWaves = 4;  // waves per workgroup in the matrix-core kernel
 constexpr int kRowsSub = 2;    // 16-key subtiles per wave there
 
-static int pick_rg(int num_rows, int num_req) {
-  const int avg = (num_rows + num_req - 1) / num_req;
-  return avg <= 1 ? 1 : avg <= 2 ? 2 : avg <= 4 ? 4 : 8;
-}
+// Rows per request (rounded up) pick the kernel: 1 or 2 -> the VALU kernel
+// with that many rows per pass; more -> the matrix-core kernel.
+static int rows_per_request(int num_rows, int num_req) { return (num_rows + num_req - 1) / num_req; }
 
 int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_pages,
                         const int32_t* page_table, int32_t pt_stride,
@@ -312,8 +310,8 @@ int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_p
   const int64_t chunk = keys >= (1 << 18) ? 128 : 64;
   const int nchunks = max_vis > 0 ? (int)((max_vis + chunk - 1) / chunk) : 1;
   dim3 grid(nchunks, num_req), block(256);
-  const int rg = pick_rg(num_rows, num_req);
-  if (rg >= 4) {
+  const int avg = rows_per_request(num_rows, num_req);
+  if (avg > 2) {
     // Several rows per request: the matrix-core kernel, 64*KSUB-key chunks.
     constexpr int P = kRowsSub, W = kRowsWaves, kChunkM = 16 * W * P;
     // Two chunks per workgroup: with ragged requests most workgroups of the
@@ -322,7 +320,6 @@ int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_p
     // chunks: 36.7 us).
     constexpr int kFold = 2;
     const int nch = max_vis > 0 ? ((max_vis + kChunkM - 1) / kChunkM + kFold - 1) / kFold : 1;
-    const int avg = (num_rows + num_req - 1) / num_req;
     dim3 gm(nch, num_req);
     if (avg <= 4)
       hipLaunchKernelGGL((score_rows_mfma_kernel<1, W, P>), gm, dim3(64 * W), 0, stream, q, kcache, num_pages, page_table,
@@ -335,17 +332,12 @@ int launch_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_p
                          pt_stride, req_row_ptr, row_pos, c, max_vis, kChunkM, kFold, scores, ld, row_len);
     return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
   }
-#define BS_LAUNCH_DECODE(RGV)                                                                 \
-  hipLaunchKernelGGL((score_decode_kernel<RGV, U>), grid, block, 0, stream, q, kcache, num_pages, \
-                     page_table, pt_stride, req_row_ptr, row_pos, c, max_vis, (int32_t)chunk,    \
-                     scores, ld, row_len)
-  switch (rg) {
-    case 1: BS_LAUNCH_DECODE(1); break;
-    case 2: BS_LAUNCH_DECODE(2); break;
-    case 4: BS_LAUNCH_DECODE(4); break;
-    default: BS_LAUNCH_DECODE(8); break;
-  }
-#undef BS_LAUNCH_DECODE
+  if (avg <= 1)
+    hipLaunchKernelGGL((score_decode_kernel<1, U>), grid, block, 0, stream, q, kcache, num_pages, page_table,
+                       pt_stride, req_row_ptr, row_pos, c, max_vis, (int32_t)chunk, scores, ld, row_len);
+  else
+    hipLaunchKernelGGL((score_decode_kernel<2, U>), grid, block, 0, stream, q, kcache, num_pages, page_table,
+                       pt_stride, req_row_ptr, row_pos, c, max_vis, (int32_t)chunk, scores, ld, row_len);
   return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
 }
 

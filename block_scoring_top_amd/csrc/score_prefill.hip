@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
 
   if (row_len != nullptr)
     for (int64_t r = (int64_t)blockIdx.x * 256 + tid; r < num_rows; r += (int64_t)gridDim.x * 256)
-      row_len[r] = max(0, min((row_pos[r] + 1) / c, max_vis));
+      row_len[r] = visible_blocks(row_pos[r], c, max_vis);
 
   // This workgroup's contiguous range of units.
   const int64_t u0 = units * blockIdx.x / gridDim.x;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(
     // 0 past the block): the block's longest bounds its tiles; each lane
     // takes those of the 4 rows it stores by shuffle; the wave's shortest
     // decides which tiles store without masks.
-    const int nv_lane = lane < rb1 - rb0 ? max(0, min((row_pos[rb0 + lane] + 1) / c, max_vis)) : 0;
+    const int nv_lane = lane < rb1 - rb0 ? visible_blocks(row_pos[rb0 + lane], c, max_vis) : 0;
     int nmax = nv_lane;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off));

@@ -17,26 +17,29 @@
 //
 // CDNA4 has no thread-block clusters or distributed shared memory.  The
 // blog's paths become:
-//   * rows that are not few-and-long: one workgroup per row, the row held in
-//     registers, 1,024 lanes x 16 values (longer rows streamed twice), or,
-//     for batches of at least 1,024 rows of at most 16,384 entries, 256 lanes
-//     x 64 values so that several rows share a CU.  The register path keeps
-//     each entry's bin, not its value, and marks the entries above and in the
-//     boundary bin with two bit masks;
-//   * few long rows (>= 32,769 entries, at most 256 rows): one 256-lane
-//     workgroup per 2,048-entry chunk (8 entries per lane, in registers).
-//     A first launch merges the chunks' LDS histograms into the row's
-//     histogram with device atomics.  In a second launch every chunk finds
-//     the threshold bin, emits and translates its own above-threshold entries
-//     and appends its boundary-bin entries to the row's candidate list; the
-//     last chunk to arrive (a device-scope counter) resolves the boundary bin
-//     from that list.  No workgroup waits on another (no co-residency
-//     assumption) and no device-scope fence is issued: on gfx950 such a fence
-//     writes back and invalidates the per-XCD L2, which measured far costlier
-//     than the whole kernel.  Data crossing workgroups inside a launch (the
-//     candidate list, the counters) moves only through device-scope atomic
-//     loads and stores, performed at the device coherence point; each chunk
-//     waits for its stores to complete before it arrives;
+//   * rows shorter than 32,769 entries: one workgroup per row, the row held
+//     in registers, 1,024 lanes x 16 values (longer rows streamed twice), or
+//     512 lanes x 64 values for rows of up to 32,768 entries, or, for batches
+//     of at least 1,024 rows of at most 16,384 entries, 256 lanes x 64 values
+//     so that several rows share a CU.  The register path keeps each entry's
+//     bin, not its value, and marks the entries above and in the boundary bin
+//     with two bit masks;
+//   * long rows (>= 32,769 entries, any number of rows): one launch, one
+//     1,024-lane workgroup per 16,384-entry chunk, the chunk in registers.
+//     In place of the cluster's merged histogram, each chunk builds its own
+//     histogram and keeps as candidates every entry at or above the bin of
+//     its local q-th largest, q a little above the chunk's expected share of
+//     the row's top k; it publishes them with their bin floor and arrives on
+//     the row's counter.  The last chunk to arrive merges the candidates'
+//     histogram in LDS, finds the threshold bin, emits the entries above it
+//     and refines the boundary bin exactly.  The candidates are the whole row
+//     at and above the threshold bin whenever that bin is not below any
+//     chunk's floor (checked; otherwise the same workgroup selects the whole
+//     row by streaming it), so the result is exact in every case.  No
+//     workgroup waits on another (no co-residency assumption) and no
+//     device-scope fence is issued: on gfx950 such a fence writes back and
+//     invalidates the per-XCD L2, which measured far costlier than the whole
+//     kernel;
 //   * emission is count, block scan, write (no per-entry atomics); the
 //     threshold scan runs on one wave with DPP scans; the boundary
 //     refinement costs one workgroup barrier per 8-bit radix pass.
@@ -55,29 +58,62 @@ constexpr int kManyNT = 256;                   // row kernel for many rows: lane
 constexpr int kManyVpt = 64;                   // ...values per lane in registers
 constexpr int kManyCand = 1024;                // ...boundary candidates in LDS
 constexpr int kManyMinRows = 1024;             // batches with at least this many rows
-constexpr int kLongNT = 256;                   // lanes per workgroup on the long-row kernels
-constexpr int kLongVpt = 16;                   // values per lane held at once there
-constexpr int kLongCand = 4096;
-constexpr int kLongMin = 32769;                // rows this long use several workgroups...
-constexpr int kLongRowsMax = 256;              // ...when the batch has at most this many rows
-constexpr int kChunk = 2048;                   // entries per workgroup on long rows (a sweep of 1,024-16,384 on 16 x 81,920 rows: 2,048 fastest)
-constexpr int kPerLane = kChunk / kLongNT;     // 8
-constexpr int kHistChunk = 4096;               // entries per workgroup in the long-row histogram launch (2,048-8,192 measured alike)
-constexpr int kHistPerLane = kHistChunk / kLongNT;
-static_assert(kHistChunk % (2 * kLongNT) == 0, "histogram chunks are whole lane pairs");
-constexpr int kChunkPages = 4 * kChunk / kPage;  // logical pages a chunk's blocks span (c <= 4)
-constexpr int kRowPages = 1024;                  // a row's first page ids, cached in LDS for its translation
-static_assert(kChunk % kLongNT == 0, "a long-row chunk is a whole number of lanes");
+constexpr int kLongMin = 32769;                // rows this long are split over several workgroups
+constexpr int kCkNT = 512;                     // long rows: lanes per workgroup (1,024 measured slower)
+constexpr int kCkVpt = 16;                     // ...values per lane
+constexpr int kCkChunk = kCkNT * kCkVpt;       // ...entries per chunk (one workgroup each)
+constexpr int kCkCand = 4096;                  // ...boundary-bin candidates the resolving workgroup holds
+constexpr int kCkAll = 8192;                   // ...chunk candidates it holds in registers
+constexpr int kCkMeta = 1024;                  // ...chunks per row it can track
+constexpr int kRowPages = 1024;                // a row's first page ids, cached in LDS for its translation
+constexpr int kCkPages = 4096;                 // the same on long rows
 
-// Workspace record per row (long rows only): merged histogram, counters
-// ([0] arrivals, [1] emitted above the threshold, [2] boundary candidates),
-// boundary candidate list.
-constexpr size_t kWsHist = 0;
-constexpr size_t kWsCtr = kBins * 4;
-constexpr size_t kWsCand = kWsCtr + 64;
-constexpr size_t kWsRow = kWsCand + (size_t)kLongCand * 8;
+// Candidates a long-row chunk of CH entries keeps: e = its expected share of
+// the row's top k (rounded up), plus 4 standard deviations of a binomial
+// count and 16.  Non-increasing in n.  Host and device compute it alike
+// (integers only; CH*k + n fits 32 bits for every admitted row).
+__host__ __device__ __forceinline__ constexpr int ck_isqrt_ceil(int e) {
+  int s = 0;
+  while (s * s < e) ++s;
+  return s;
+}
+template <int CH>
+__host__ __device__ __forceinline__ constexpr int ck_quota(int64_t n, int k) {
+  const int e = (int)(((uint32_t)CH * (uint32_t)k + (uint32_t)n - 1u) / (uint32_t)n);
+  return e + 4 * ck_isqrt_ceil(e) + 16;
+}
+// Candidate slots per chunk for quota q: the quota plus room for the rest of
+// the bin the q-th largest falls in (a chunk whose candidates would overflow
+// them keeps only the bins above; the resolver then finds a floor above its
+// threshold).
+__host__ __device__ __forceinline__ constexpr int ck_slots_for(int q) { return (q + q / 8 + 32 + 31) / 32 * 32; }
+template <int CH>
+__host__ __device__ __forceinline__ constexpr int ck_slots(int64_t n, int k) {
+  return ck_slots_for(ck_quota<CH>(n, k));
+}
+// An unused candidate slot: no real candidate has this pattern (its index
+// would be 2^32 - 1).
+constexpr uint64_t kNoCand = ~0ull;
+static_assert(kCkChunk <= 65535, "a chunk's per-bin counts fit 16 bits");
 
-template <int CAP>
+// Workspace record per long row: counters ([0] arrivals), each chunk's
+// packed (candidate count << 16 | bin floor), each chunk's histogram at and
+// above its floor (16-bit counts, zeros below), each chunk's candidates (FP32
+// bits << 32 | index, then unused markers) at chunk * ck_slots(n, k).
+constexpr size_t kWsCtr = 0;
+constexpr size_t kWsMeta = 64;
+__host__ __device__ constexpr size_t ck_meta_bytes(int wmax) { return ((size_t)wmax * 4 + 255) / 256 * 256; }
+__host__ __device__ constexpr size_t ck_hist_offset(int wmax) { return kWsMeta + ck_meta_bytes(wmax); }
+__host__ __device__ constexpr size_t ck_cand_offset(int wmax) {
+  return ck_hist_offset(wmax) + (size_t)wmax * kBins * 2;
+}
+static size_t ck_record_bytes(int32_t max_len, int32_t k) {
+  const int wmax = (max_len + kCkChunk - 1) / kCkChunk;
+  const size_t b = ck_cand_offset(wmax) + (size_t)wmax * ck_slots<kCkChunk>(kLongMin, k) * 8;
+  return (b + 255) / 256 * 256;
+}
+
+template <int CAP, int RP = kRowPages>
 struct TopkShared {
   uint32_t hist[kBins];
   uint32_t digit[256];
@@ -88,10 +124,10 @@ struct TopkShared {
   uint32_t T;
   uint32_t above;
   uint32_t last;
-  uint32_t base_up, base_cand;
+  uint32_t bmax;
+  uint32_t inbin;
   uint64_t red_and[16], red_or[16];
-  int32_t pages[kChunkPages];  // page ids of a long-row chunk's token range (fused translation)
-  int32_t row_pages[kRowPages];  // page ids 0 .. row_npages-1 of a whole row's request (fused translation)
+  int32_t row_pages[RP];  // page ids 0 .. row_npages-1 of a whole row's request (fused translation)
   uint32_t row_npages;
 };
 
@@ -155,6 +191,17 @@ __device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, bool p) {
   return base + lanes_below(mask);
 }
 
+// Reserves cnt consecutive slots per lane (any cnt >= 0) from *counter with
+// one LDS atomic per wave; returns this lane's first slot.  All 64 lanes must
+// call.
+__device__ __forceinline__ uint32_t wave_reserve_n(uint32_t* counter, uint32_t cnt) {
+  const uint32_t incl = wave_incl_scan(cnt);
+  uint32_t base = 0;
+  if (lane_id() == 63) base = atomicAdd(counter, incl);
+  base = readlane(base, 63);
+  return base + incl - cnt;
+}
+
 // One wave: over the NB counts h[0..NB) (NB a power of two <= 1024), the
 // largest bin T whose suffix count reaches m, and the count strictly above
 // T.  Lane L owns the L-th group of NB/64 bins from the top.  Returns T = 0,
@@ -191,8 +238,8 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* h, uint32_t m, ui
 
 // Block-wide exclusive prefix sum of one value per lane (all lanes call);
 // `total` gets the block's sum.  Two barriers.
-template <int NT, int CAP>
-__device__ __forceinline__ uint32_t block_excl_scan(TopkShared<CAP>& s, uint32_t x, uint32_t& total) {
+template <int NT, int CAP, int RP>
+__device__ __forceinline__ uint32_t block_excl_scan(TopkShared<CAP, RP>& s, uint32_t x, uint32_t& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(x);
   if (lane == 63) s.wave_tot[wave] = incl;
@@ -209,18 +256,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(TopkShared<CAP>& s, uint32_t
   return off + incl - x;
 }
 
-// Translation of the refinement's winners as they are emitted: a winner at
-// selection position q holding block j fills output entries q*c .. q*c+c-1
-// (positions c*j + u, slots page*64 + (c*j + u) mod 64, page read from the
-// request's page-table row; -1 for an invalid block or page).  pt == nullptr:
-// no translation.
-struct WinnerTr {
-  const int32_t* pt;
-  int c, nv, pt_stride;
-  int32_t* orow;
-  int32_t* prow;  // may be nullptr
-};
-
 // The whole workgroup resolves the boundary bin from s.cand[0..nc) (nc > need
 // >= 1, nc <= CAP): each lane holds up to PER candidates in registers
 // (candidate i*NT + lane).  An exact MSB-first radix selection on the 64-bit
@@ -230,18 +265,14 @@ struct WinnerTr {
 // buffers rotate (in s.hist, free once the threshold bin is known), so one
 // barrier per pass suffices: the buffer pass p + 1 fills was last read in
 // pass p - 2 and is cleared during pass p.  The `need` winners are
-// emitted by count, block scan, write at out[base ...] (and chosen[base ...]);
-// with translation each lane reads the page ids of its own candidates before
-// the passes and writes the winners' slots as it emits them.
-template <int NT, int CAP, int PER>
-__device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc, uint32_t need,
-                                                 int32_t* __restrict__ out, int32_t* chosen, uint32_t base, int limit,
-                                                 const WinnerTr& wt) {
+// emitted by count, block scan, write at out[base ...] (and chosen[base ...]).
+template <int NT, int CAP, int RP, int PER>
+__device__ __forceinline__ void block_refine_per(TopkShared<CAP, RP>& s, uint32_t nc, uint32_t need,
+                                                 int32_t* __restrict__ out, int32_t* chosen, uint32_t base, int limit) {
   static_assert(3 * 256 <= kBins, "three digit buffers fit in the histogram's storage");
   const int tid = threadIdx.x, wave = tid >> 6;
   uint32_t* const dig = s.hist;
   uint64_t key[PER];
-  int pg[PER];
   uint64_t a = ~0ull, o = 0ull;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -250,15 +281,6 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc
     if (j < nc) {
       a &= key[i];
       o |= key[i];
-    }
-  }
-  if (wt.pt) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = index_of(key[i]);
-      const int p0 = wt.c * idx;
-      pg[i] = -1;
-      if ((uint32_t)(i * NT + tid) < nc && idx >= 0 && idx < wt.nv && (p0 >> 6) < wt.pt_stride) pg[i] = wt.pt[p0 >> 6];
     }
   }
   a = wave_and64(a);
@@ -316,14 +338,6 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc
         const int idx = index_of(key[i]);
         if (out) out[pos] = idx;
         if (chosen) chosen[pos] = idx;
-        if (wt.pt) {
-          const bool valid = idx >= 0 && idx < wt.nv;
-          const int p0 = wt.c * idx;
-          for (int u = 0; u < wt.c; ++u) {
-            wt.orow[pos * wt.c + u] = pg[i] >= 0 ? pg[i] * kPage + ((p0 + u) & (kPage - 1)) : -1;
-            if (wt.prow) wt.prow[pos * wt.c + u] = valid ? p0 + u : -1;
-          }
-        }
       }
       ++pos;
     }
@@ -341,8 +355,8 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP>& s, uint32_t nc
 // throughput is the limit, the radix passes measured slightly faster.
 constexpr int kRankMax = 256;
 
-template <int NT, int CAP>
-__device__ __forceinline__ void rank_refine(TopkShared<CAP>& s, uint32_t nc, uint32_t need,
+template <int NT, int CAP, int RP>
+__device__ __forceinline__ void rank_refine(TopkShared<CAP, RP>& s, uint32_t nc, uint32_t need,
                                             int32_t* __restrict__ out, int32_t* chosen, uint32_t base) {
   const uint32_t tid = threadIdx.x;
   if (tid < nc) {
@@ -360,22 +374,21 @@ __device__ __forceinline__ void rank_refine(TopkShared<CAP>& s, uint32_t nc, uin
   }
 }
 
-template <int NT, int CAP>
-__device__ __forceinline__ void block_refine(TopkShared<CAP>& s, uint32_t nc, uint32_t need, int32_t* __restrict__ out,
-                                             int32_t* chosen, uint32_t base, int limit,
-                                             const WinnerTr& wt = WinnerTr{}) {
+template <int NT, int CAP, int RP>
+__device__ __forceinline__ void block_refine(TopkShared<CAP, RP>& s, uint32_t nc, uint32_t need, int32_t* __restrict__ out,
+                                             int32_t* chosen, uint32_t base, int limit) {
   constexpr int PMAX = (CAP + NT - 1) / NT;
-  if (PMAX > 1 && nc <= (uint32_t)NT) block_refine_per<NT, CAP, 1>(s, nc, need, out, chosen, base, limit, wt);
-  else if (PMAX > 2 && nc <= 2u * NT) block_refine_per<NT, CAP, 2>(s, nc, need, out, chosen, base, limit, wt);
-  else if (PMAX > 4 && nc <= 4u * NT) block_refine_per<NT, CAP, 4>(s, nc, need, out, chosen, base, limit, wt);
-  else block_refine_per<NT, CAP, PMAX>(s, nc, need, out, chosen, base, limit, wt);
+  if (PMAX > 1 && nc <= (uint32_t)NT) block_refine_per<NT, CAP, RP, 1>(s, nc, need, out, chosen, base, limit);
+  else if (PMAX > 2 && nc <= 2u * NT) block_refine_per<NT, CAP, RP, 2>(s, nc, need, out, chosen, base, limit);
+  else if (PMAX > 4 && nc <= 4u * NT) block_refine_per<NT, CAP, RP, 4>(s, nc, need, out, chosen, base, limit);
+  else block_refine_per<NT, CAP, RP, PMAX>(s, nc, need, out, chosen, base, limit);
 }
 
 // Block-wide fallback when the boundary bin overflows the LDS list: radix
 // passes re-read the row (entries in bin T), the digit histogram is built by
 // every lane, the decisions are taken by wave 0.  Rare (tie storms).
-template <int NT, int CAP>
-__device__ __forceinline__ void block_refine_from_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, uint32_t T,
+template <int NT, int CAP, int RP>
+__device__ __forceinline__ void block_refine_from_row(TopkShared<CAP, RP>& s, const float* __restrict__ row, int n, uint32_t T,
                                       uint32_t need, int32_t* __restrict__ out, int32_t* chosen, int limit) {
   __shared__ uint64_t red_and[NT / 64], red_or[NT / 64];
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -460,8 +473,8 @@ __device__ __forceinline__ void block_refine_from_row(TopkShared<CAP>& s, const 
 // block scan of the packed counts (above << 20 | boundary) hands out the
 // positions, then plain writes: no atomics.  up_pos / cand_pos carry the
 // running totals across tiles.
-template <int NT, int V, int CAP>
-__device__ __forceinline__ void emit_tile(TopkShared<CAP>& s, float (&x)[V], int base, int n, uint32_t T,
+template <int NT, int V, int CAP, int RP>
+__device__ __forceinline__ void emit_tile(TopkShared<CAP, RP>& s, float (&x)[V], int base, int n, uint32_t T,
                                           uint32_t& up_pos, uint32_t& cand_pos, int m, int32_t* __restrict__ out,
                                           bool keep) {
   uint32_t nup = 0, neq = 0;
@@ -498,8 +511,8 @@ __device__ __forceinline__ void emit_tile(TopkShared<CAP>& s, float (&x)[V], int
   cand_pos += total & 0xFFFFFu;
 }
 
-template <int CAP>
-__device__ __forceinline__ void threshold_to_shared(TopkShared<CAP>& s, uint32_t m) {
+template <int CAP, int RP>
+__device__ __forceinline__ void threshold_to_shared(TopkShared<CAP, RP>& s, uint32_t m) {
   if ((threadIdx.x >> 6) == 0) {
     uint32_t T, ab;
     wave_threshold<kBins>(s.hist, m, T, ab);
@@ -511,13 +524,58 @@ __device__ __forceinline__ void threshold_to_shared(TopkShared<CAP>& s, uint32_t
   __syncthreads();
 }
 
+// Block-wide threshold over the 1,024 bins, held B = 1024/NT per lane from
+// the top (lane i owns bins 1023 - B*i down to 1024 - B*(i+1); c[j] is the
+// count of bin 1023 - B*i - j): the largest bin T whose suffix count reaches
+// m, the count strictly above T and the count in T.  One DPP scan per wave,
+// the wave totals through LDS: two barriers, no serial wave.  T = above =
+// inbin = 0 if no bin qualifies (m above the total).  All lanes call.
+template <int NT, int CAP, int RP>
+__device__ __forceinline__ void block_threshold(TopkShared<CAP, RP>& s, const uint32_t (&c)[kBins / NT], uint32_t m,
+                                                uint32_t& T, uint32_t& above, uint32_t& inbin) {
+  constexpr int B = kBins / NT;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < B; ++i) t += c[i];
+  const uint32_t incl = wave_incl_scan(t);
+  if (lane == 63) s.wave_tot[wave] = incl;
+  if (tid == 0) {
+    s.T = 0;
+    s.above = 0;
+    s.inbin = 0;
+  }
+  __syncthreads();
+  uint32_t off = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) off += w < wave ? s.wave_tot[w] : 0u;
+  uint32_t acc = off + incl - t;  // entries in the bins above this lane's
+  if (acc < m && acc + t >= m) {
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if (!found && acc + c[i] >= m) {
+        s.T = (uint32_t)(kBins - 1 - B * tid - i);
+        s.above = acc;
+        s.inbin = c[i];
+        found = true;
+      }
+      acc += c[i];
+    }
+  }
+  __syncthreads();
+  T = s.T;
+  above = s.above;
+  inbin = s.inbin;
+}
+
 // One workgroup selects a whole row with n > m.  Rows of up to NT*V entries
 // are read once and held in registers; longer rows are streamed: once for
 // the histogram (skipped when it is ready), once in NT*V-entry tiles for
 // emission.  HIST_READY: s.hist
 // already holds the row's histogram (long-row finisher).  All lanes call.
-template <int NT, int V, int CAP, bool HIST_READY, bool STREAM, class PF>
-__device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m,
+template <int NT, int V, int CAP, int RP, bool HIST_READY, bool STREAM, class PF>
+__device__ __forceinline__ void select_row(TopkShared<CAP, RP>& s, const float* __restrict__ row, int n, int m,
                                            int32_t* __restrict__ out, bool keep, PF& pf) {
   constexpr int kTile = V;
   const int tid = threadIdx.x;
@@ -676,18 +734,6 @@ __device__ __forceinline__ void select_row(TopkShared<CAP>& s, const float* __re
   }
 }
 
-// Request of row r: the number of request starts at or before r, minus one.
-// All 64 lanes of the calling wave must call.
-__device__ __forceinline__ int request_of(const int32_t* __restrict__ req_row_ptr, int num_req, int r) {
-  int b = -1;
-  for (int base = 0; base < num_req; base += 64) {
-    const int bi = base + lane_id();
-    const bool started = bi < num_req && req_row_ptr[bi] <= r;
-    b += __popcll(__ballot(started));
-  }
-  return max(0, min(b, num_req - 1));
-}
-
 // Fused translation.  Selection position q of row r holding block j becomes
 // output entries q*c .. q*c+c-1 (positions c*j .. c*j+c-1); after the m
 // chosen blocks come the pending positions c*n_vis .. t, then -1.  slot =
@@ -696,17 +742,8 @@ struct RowGeom {
   int b, t, nv, p;
 };
 
-__device__ __forceinline__ RowGeom row_geometry(const Translate& tr, int r) {
-  RowGeom g;
-  g.b = request_of(tr.req_row_ptr, tr.num_req, r);
-  g.t = tr.row_pos[r];
-  g.nv = g.t >= 0 ? (g.t + 1) / tr.c : 0;
-  g.p = g.t >= 0 ? g.t + 1 - tr.c * g.nv : 0;
-  return g;
-}
-
-// The same, split so that its reads can be issued long before the values
-// are needed: start() reads the row's position and the first 64 request
+// A row's request, position, visible blocks and pending count, split so
+// that its reads can be issued long before the values are needed: start() reads the row's position and the first 64 request
 // starts (one per lane), finish() turns them into the geometry (all 64
 // lanes of each wave call both; requests past the first 64 are read there).
 struct RowGeomReads {
@@ -732,40 +769,6 @@ __device__ __forceinline__ RowGeom row_geometry_finish(const Translate& tr, int 
   return g;
 }
 
-__device__ __forceinline__ void put_slot(const Translate& tr, const RowGeom& g, int r, int i, int pos) {
-  int slot = -1;
-  if (pos >= 0 && (pos >> 6) < tr.pt_stride) {
-    const int page = tr.page_table[(int64_t)g.b * tr.pt_stride + (pos >> 6)];
-    slot = page >= 0 ? page * kPage + (pos & (kPage - 1)) : -1;
-  }
-  tr.out_slots[(int64_t)r * tr.ld_out + i] = slot;
-  if (tr.out_pos) tr.out_pos[(int64_t)r * tr.ld_out + i] = pos;
-}
-
-// Output entries of selection position q (block j): the block's c positions
-// lie in one page, so one page-table read serves them all.
-__device__ __forceinline__ void translate_block(const Translate& tr, const RowGeom& g, int r, int q, int j) {
-  const int c = tr.c;
-  const bool valid = j >= 0 && j < g.nv;
-  const int p0 = c * j;
-  int page = -1;
-  if (valid && (p0 >> 6) < tr.pt_stride) page = tr.page_table[(int64_t)g.b * tr.pt_stride + (p0 >> 6)];
-  int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out + q * c;
-  int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out + q * c : nullptr;
-  for (int u = 0; u < c; ++u) {
-    orow[u] = page >= 0 ? page * kPage + ((p0 + u) & (kPage - 1)) : -1;
-    if (prow) prow[u] = valid ? p0 + u : -1;
-  }
-}
-
-// Output entries from m*c on: the pending tail, then -1; and the count.
-template <int NT>
-__device__ __forceinline__ void translate_tail(const Translate& tr, const RowGeom& g, int r, int m) {
-  const int nblk = tr.c * m, total = nblk + g.p;
-  for (int i = nblk + (int)threadIdx.x; i < tr.ld_out; i += NT) put_slot(tr, g, r, i, i < total ? tr.c * g.nv + (i - nblk) : -1);
-  if (threadIdx.x == 0) tr.out_count[r] = total;
-}
-
 // The whole row from chosen[0..m).  Element-major: lane l handles output
 // entries l, l + NT, l + 2*NT, ..., so every store instruction of a wave
 // covers 256 contiguous bytes; entry i < c*m belongs to selection position
@@ -785,33 +788,61 @@ __device__ __forceinline__ void translate_rounds(const Translate& tr, const RowG
   const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
   int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out;
   int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out : nullptr;
-  for (int i0 = 0; i0 < tr.ld_out; i0 += E * NT) {
-    int pos[E], page[E];
+  if (CACHED) {
+    // Branch-free: a round's selection reads, then its page-id reads, are
+    // issued together (indices clamped into range, results unused where they
+    // do not apply), and the stores go through buffer resources whose range
+    // check drops entries at or past ld_out (and every position store when
+    // there is no position output).
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(orow, (short)0, tr.ld_out * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(prow ? prow : orow, (short)0, prow ? tr.ld_out * 4 : 0, 0x00020000);
+    const int mlast = max(m - 1, 0);
+    for (int i0 = 0; i0 < tr.ld_out; i0 += E * NT) {
+      int j[E], ps[E], pg[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = i0 + e * NT + (int)threadIdx.x;
-      int ps = -1;
-      if (i < nblk) {
-        const int j = chosen[i >> sh];
-        if (j >= 0 && j < g.nv) ps = c * j + (i & (c - 1));
-      } else if (i < total) {
-        ps = c * g.nv + (i - nblk);
+      for (int e = 0; e < E; ++e) j[e] = chosen[min((i0 + e * NT + (int)threadIdx.x) >> sh, mlast)];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = i0 + e * NT + (int)threadIdx.x;
+        const int pb = j[e] >= 0 && j[e] < g.nv ? c * j[e] + (i & (c - 1)) : -1;
+        ps[e] = i < nblk ? pb : i < total ? c * g.nv + (i - nblk) : -1;
       }
-      int pg = -1;
-      if (CACHED) {
-        if (ps >= 0) pg = cached[ps >> 6];
-      } else if (ps >= 0 && (ps >> 6) < tr.pt_stride) {
-        pg = (ps >> 6) < ncached ? cached[ps >> 6] : pt[ps >> 6];
+#pragma unroll
+      for (int e = 0; e < E; ++e) pg[e] = cached[max(ps[e], 0) >> 6];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t off = (uint32_t)(i0 + e * NT + (int)threadIdx.x) * 4u;
+        const int slot = ps[e] >= 0 && pg[e] >= 0 ? pg[e] * kPage + (ps[e] & (kPage - 1)) : -1;
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)slot, ors, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)ps[e], prs, off, 0, 0);
       }
-      pos[e] = ps;
-      page[e] = pg;
     }
+  } else {
+    for (int i0 = 0; i0 < tr.ld_out; i0 += E * NT) {
+      int pos[E], page[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = i0 + e * NT + (int)threadIdx.x;
-      if (i < tr.ld_out) {
-        orow[i] = page[e] >= 0 ? page[e] * kPage + (pos[e] & (kPage - 1)) : -1;
-        if (prow) prow[i] = pos[e];
+      for (int e = 0; e < E; ++e) {
+        const int i = i0 + e * NT + (int)threadIdx.x;
+        int ps = -1;
+        if (i < nblk) {
+          const int j = chosen[i >> sh];
+          if (j >= 0 && j < g.nv) ps = c * j + (i & (c - 1));
+        } else if (i < total) {
+          ps = c * g.nv + (i - nblk);
+        }
+        int pg = -1;
+        if (ps >= 0 && (ps >> 6) < tr.pt_stride) pg = (ps >> 6) < ncached ? cached[ps >> 6] : pt[ps >> 6];
+        pos[e] = ps;
+        page[e] = pg;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = i0 + e * NT + (int)threadIdx.x;
+        if (i < tr.ld_out) {
+          orow[i] = page[e] >= 0 ? page[e] * kPage + (pos[e] & (kPage - 1)) : -1;
+          if (prow) prow[i] = pos[e];
+        }
       }
     }
   }
@@ -831,15 +862,15 @@ __device__ __forceinline__ void translate_row(const Translate& tr, const RowGeom
     translate_rounds<NT, false>(tr, g, r, m, chosen, cached, ncached);
 }
 
-// Page ids of a row's first kRowPages logical pages, for its fused
+// Page ids of a row's first RP logical pages, for its fused
 // translation: read right after the row's scores are issued (so their
 // latency hides behind the binning) and put in LDS before the barrier that
 // follows it.  Without them the translation waited for page-table reads that
 // also waited for the selection's stores (vector memory operations retire in
 // order).  ON = false: does nothing.
-template <int NT, bool ON>
+template <int NT, bool ON, int RP = kRowPages>
 struct RowPagePrefetch {
-  static constexpr int PER = (kRowPages + NT - 1) / NT;
+  static constexpr int PER = (RP + NT - 1) / NT;
   const Translate& tr;
   int r;
   RowGeomReads gr;
@@ -849,7 +880,7 @@ struct RowPagePrefetch {
   __device__ __forceinline__ void issue() {
     if (!ON) return;
     g = row_geometry_finish(tr, r, gr);
-    np = g.t >= 0 ? min((g.t >> 6) + 1, min(kRowPages, tr.pt_stride)) : 0;
+    np = g.t >= 0 ? min((g.t >> 6) + 1, min(RP, tr.pt_stride)) : 0;
     const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -858,26 +889,26 @@ struct RowPagePrefetch {
     }
   }
   template <int CAP>
-  __device__ __forceinline__ void commit(TopkShared<CAP>& s) {
+  __device__ __forceinline__ void commit(TopkShared<CAP, RP>& s) {
     if (!ON) return;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int idx = i * NT + (int)threadIdx.x;
-      if (idx < kRowPages) s.row_pages[idx] = v[i];
+      if (idx < RP) s.row_pages[idx] = v[i];
     }
     if (threadIdx.x == 0) s.row_npages = (uint32_t)np;
   }
 };
 
 // The whole selection of one row by one workgroup, any n.
-template <int NT, int VPT, int CAP, bool TRANSLATE, bool STREAM = true>
-__device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float* __restrict__ row, int n, int m, int k,
+template <int NT, int VPT, int CAP, bool TRANSLATE, bool STREAM = true, int RP>
+__device__ __forceinline__ void select_whole_row(TopkShared<CAP, RP>& s, const float* __restrict__ row, int n, int m, int k,
                                  int32_t* __restrict__ out, int32_t* __restrict__ sel_count, int r,
                                  const Translate& tr) {
   const int tid = threadIdx.x;
   RowGeomReads gr{};
   if (TRANSLATE) gr = row_geometry_start(tr, r);  // in flight during the selection
-  RowPagePrefetch<NT, TRANSLATE> pf{tr, r, gr};
+  RowPagePrefetch<NT, TRANSLATE, RP> pf{tr, r, gr};
   // The selection is staged in LDS and written out once it is complete: a
   // global store issued early would hold up every later wait for a load
   // (vector memory operations retire in order).
@@ -886,7 +917,7 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP>& s, const float
     for (int i = tid; i < n; i += NT) s.chosen[i] = i;
     pf.commit(s);
   } else {
-    select_row<NT, VPT, CAP, false, STREAM>(s, row, n, m, nullptr, true, pf);
+    select_row<NT, VPT, CAP, RP, false, STREAM>(s, row, n, m, nullptr, true, pf);
   }
   __syncthreads();
   for (int i = tid; i < k; i += NT) out[i] = i < m ? s.chosen[i] : -1;
@@ -914,269 +945,314 @@ __global__ __launch_bounds__(NT, NT == kManyNT ? 4 : NT == kMidNT ? 2 : 1) void 
                                                           sel + (int64_t)r * k, sel_count, r, tr);
 }
 
-// Output entries of selection position q (block j of a long-row chunk),
-// page ids from the chunk's LDS copy.
-template <int C>
-__device__ __forceinline__ void translate_block_lds(const Translate& tr, int r, int q, int j, const int32_t* pages,
-                                                    int first_lp) {
-  int32_t* orow = tr.out_slots + (int64_t)r * tr.ld_out + q * C;
-  int32_t* prow = tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out + q * C : nullptr;
-#pragma unroll
-  for (int u = 0; u < C; ++u) {
-    const int pos = C * j + u;
-    const int page = pages[(pos >> 6) - first_lp];
-    orow[u] = page >= 0 ? page * kPage + (pos & (kPage - 1)) : -1;
-    if (prow) prow[u] = pos;
-  }
+// Long rows, one launch.  Every workgroup holds the row kernels' shared
+// memory (histogram, boundary list, selection, a page cache sized for long
+// rows).
+struct ChunkShared {
+  TopkShared<kCkCand, kCkPages> t;
+  int32_t trash32[kCkNT];   // per-lane targets of writes that do not apply
+  uint64_t trash64[kCkNT];
+};
+
+// Data crossing workgroups inside the launch (a chunk's candidates,
+// histogram and packed floor/count, the arrival counter) moves only through
+// device-scope atomic loads and stores with relaxed order.  On gfx950 these
+// are performed at the device coherence point rather than in a workgroup's
+// XCD-local L2, and a store decrements the vector memory counter only once
+// it has been performed there, so "s_waitcnt vmcnt(0)" after a chunk's
+// stores and before its arrival means: every store is visible to any
+// device-scope load issued after the arrival is counted.  The resolving
+// workgroup issues its loads only after its own arrival returned the final
+// count.  A release/acquire pair would also order these, but at device scope
+// it compiles to a write-back (and, for acquire, an invalidation) of the
+// whole per-XCD L2, which measured far costlier than the kernel; nothing here
+// relies on plain (L2-cached) stores becoming visible inside the launch.
+__device__ __forceinline__ void ws_store32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ws_store64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same store through a buffer resource (cache policy sc1, which is what
+// the device-scope store above compiles to): low word lo, high word hi at
+// byte offset off; offsets at or past the resource's range are dropped.
+typedef uint32_t bs_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void ws_buffer_store64(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t lo, uint32_t hi) {
+  constexpr int kSc1 = 16;
+  __builtin_amdgcn_raw_buffer_store_b64(bs_u32x2{lo, hi}, rs, off, 0, kSc1);
+}
+__device__ __forceinline__ uint32_t ws_load32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ws_load64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Few long rows, first launch: one 256-lane workgroup per 4,096-entry chunk
-// merges its LDS histogram into the row's histogram with device atomics.
-// Rows shorter than kLongMin are done whole by their first workgroup.
-template <bool TRANSLATE>
-__global__ __launch_bounds__(kLongNT) void topk_long_hist_kernel(
+// Rows of >= kLongMin entries: one workgroup per CH = NT*16-entry chunk
+// (grid y); shorter rows are selected whole by their first workgroup.
+//
+// Chunk phase.  The chunk's 16 values per lane stay in registers (loaded
+// before the row's length is known, within max_len); their bins go into an
+// LDS histogram.  With q = min(ck_quota(n, k), chunk length), the chunk's
+// floor is the bin of its q-th largest entry, and every entry at or above
+// the floor is a candidate.  If those would not fit in the chunk's slots, the
+// floor moves one bin up (fewer than q candidates); if the chunk keeps every
+// entry, its floor is 0.  It publishes its histogram at and above the floor,
+// its candidates (staged in LDS, stored coalesced) and (count, floor), waits
+// for those stores and arrives on the row's counter.
+//
+// Resolution, by the last chunk to arrive.  Let U be the union of the
+// candidates and T the threshold bin of U for k (from the sum of the
+// published histograms).  Each chunk's candidates are all of its entries at
+// or above its floor, so when T is at or above every floor, U holds every
+// entry of the row in bins >= T: the row's own threshold is T, its
+// above-threshold entries and its boundary bin are U's, and selecting within
+// U is exact.  Otherwise (a chunk holding more of the row's top than its
+// quota) the workgroup selects the whole row itself, streaming it.  The
+// candidates are read back in one round trip (every chunk's slot range,
+// validated against the published counts), emitted above T (count, block
+// scan, LDS) and refined in bin T on the composite (FP32 key, inverted
+// index); then the selection is written out and translated, and the row's
+// arrival counter is reset for the next call.
+template <bool TRANSLATE, int NT>
+__global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
     int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
-    Translate tr) {
-  __shared__ TopkShared<kLongCand> s;
+    int64_t rec_bytes, int32_t wmax, Translate tr) {
+  constexpr int VPT = kCkVpt, CH = NT * VPT, B = kBins / NT, P = VPT / 2, PA = kCkAll / NT;
+  static_assert(B == 2, "the published histogram packs each lane's two bins into one 32-bit store");
+  static_assert(CH <= 65535, "a chunk's per-bin counts fit 16 bits");
+  __shared__ ChunkShared cs;
+  TopkShared<kCkCand, kCkPages>& s = cs.t;
   const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x;
-  const int n = max(0, min(row_len[r], max_len));
-  const int m = min(k, n);
+  const int lo = w * CH;
   const float* row = scores + (int64_t)r * ld;
+  // The chunk's loads go out with the row-length read (the row holds
+  // max_len readable entries); entries at or past the length are masked.
+  const RowReader rdx(row, max_len);
+  float x[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) x[i] = rdx.at(tid, lo + i * NT);
+  const int n = max(0, min(row_len[r], max_len));
+  int32_t* out = sel + (int64_t)r * k;
   if (n < kLongMin) {
-    if (w == 0)
-      select_whole_row<kLongNT, kLongVpt, kLongCand, TRANSLATE>(s, row, n, m, k, sel + (int64_t)r * k, sel_count,
-                                                                 r, tr);
+    if (w == 0) select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, min(k, n), k, out, sel_count, r, tr);
     return;
   }
-  const int lo = w * kHistChunk;
   if (lo >= n) return;
-  uint32_t* gh = reinterpret_cast<uint32_t*>(ws + (size_t)r * kWsRow + kWsHist);
-  for (int i = tid; i < kBins; i += kLongNT) s.hist[i] = 0;
-  const RowReader rd(row, n);
-  float x[kHistPerLane];
-#pragma unroll
-  for (int i = 0; i < kHistPerLane; ++i) x[i] = rd.at(tid, lo + i * kLongNT);
-  __syncthreads();
-#pragma unroll
-  for (int p = 0; p < kHistPerLane / 2; ++p) {
-    const uint32_t B = bin_pair(x[2 * p], x[2 * p + 1]);
-    if (lo + (2 * p + 2) * kLongNT <= n) {  // both entries inside the row, for every lane
-      atomicAdd(&s.hist[B & 0xFFFFu], 1u);
-      atomicAdd(&s.hist[B >> 16], 1u);
-    } else {
-      if (lo + 2 * p * kLongNT + tid < n) atomicAdd(&s.hist[B & 0xFFFFu], 1u);
-      if (lo + (2 * p + 1) * kLongNT + tid < n) atomicAdd(&s.hist[B >> 16], 1u);
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < kBins; i += kLongNT) {
-    const uint32_t cnt = s.hist[i];
-    if (cnt != 0) __hip_atomic_fetch_add(&gh[i], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Few long rows, second launch.  Every chunk's workgroup reads the merged
-// histogram, finds the threshold bin, emits (and translates) its own
-// above-threshold entries through one device atomic per workgroup, and
-// appends its boundary-bin entries to the row's candidate list with
-// device-scope stores.  It waits for those stores to complete and arrives on
-// the row's counter; the last to arrive resolves the boundary bin from the
-// candidate list (read back with device-scope loads), writes the pending tail
-// and leaves the row's workspace zero-filled.  No fence, no spin.
-template <bool TRANSLATE>
-__global__ __launch_bounds__(kLongNT) void topk_long_emit_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
-    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
-    Translate tr) {
-  __shared__ TopkShared<kLongCand> s;
-  const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x;
-  const int n = max(0, min(row_len[r], max_len));
-  if (n < kLongMin) return;
-  const int lo = w * kChunk;
-  if (lo >= n) return;
-  const int nchunk = (n + kChunk - 1) / kChunk;
-  const int m = k;  // n > 2048 >= k
-  const float* row = scores + (int64_t)r * ld;
-  int32_t* out = sel + (int64_t)r * k;
-  uint8_t* rec = ws + (size_t)r * kWsRow;
-  uint32_t* gh = reinterpret_cast<uint32_t*>(rec + kWsHist);
+  const int nchunk = (n + CH - 1) / CH;
+  const int qn = ck_quota<CH>(n, k);
+  const int Q = ck_slots_for(qn);
+  const int nck = min(CH, n - lo);
+  const uint32_t q = (uint32_t)min(qn, nck);
+  uint8_t* rec = ws + (size_t)r * (size_t)rec_bytes;
   uint32_t* ctr = reinterpret_cast<uint32_t*>(rec + kWsCtr);
-  uint64_t* gcand = reinterpret_cast<uint64_t*>(rec + kWsCand);
+  uint32_t* meta = reinterpret_cast<uint32_t*>(rec + kWsMeta);
+  uint16_t* ghist = reinterpret_cast<uint16_t*>(rec + ck_hist_offset(wmax));
+  uint64_t* gcand = reinterpret_cast<uint64_t*>(rec + ck_cand_offset(wmax));
 
-  const RowReader rd(row, n);
-  float x[kPerLane];
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i) x[i] = rd[lo + i * kLongNT + tid];
-  for (int i = tid; i < kBins; i += kLongNT) s.hist[i] = gh[i];
-  RowGeom g{};
-  int first_lp = 0;
-  if (TRANSLATE) {
-    // The chunk's blocks [lo, lo + kChunk) cover at most kChunkPages logical pages.
-    g = row_geometry(tr, r);
-    first_lp = (tr.c * lo) >> 6;
-    for (int i = tid; i < kChunkPages; i += kLongNT) {
-      const int lp = first_lp + i;
-      s.pages[i] = lp < tr.pt_stride ? tr.page_table[(int64_t)g.b * tr.pt_stride + lp] : -1;
-    }
+  RowGeomReads gr{};
+  if (TRANSLATE) gr = row_geometry_start(tr, r);  // for the resolving workgroup; in flight from the start
+  for (int i = tid; i < kBins; i += NT) s.hist[i] = 0;
+  if (tid == 0) {
+    s.bmax = 0;
+    s.emit = 0;
   }
   __syncthreads();
-  threshold_to_shared(s, (uint32_t)m);
-  const uint32_t T = s.T, above = s.above;
-
-  // Count, block scan, one device atomic per list for the workgroup.
-  uint32_t nup = 0, neq = 0;
+  // Bins in pairs, kept as codes (bin + 1, 0 past the row) two per register.
+  uint32_t pb[P];
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
-    const bool valid = lo + i * kLongNT + tid < n;
-    const uint32_t b = bin_of(x[i]);
-    nup += (valid && b > T) ? 1u : 0u;
-    neq += (valid && b == T) ? 1u : 0u;
-  }
-  uint32_t total;
-  const uint32_t excl = block_excl_scan<kLongNT>(s, (nup << 20) | neq, total);
-  // The list offsets are reserved first and published after the staging
-  // below, so the atomics' round trip overlaps it.
-  uint32_t bu, bc;  // read by lane 0 only
-  if (tid == 0) {
-    bu = __hip_atomic_fetch_add(&ctr[1], total >> 20, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bc = __hip_atomic_fetch_add(&ctr[2], total & 0xFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // Stage this workgroup's picks in LDS at their scanned offsets (the
-  // running per-lane counters keep each lane's picks in index order), then
-  // write them out with all lanes: coalesced stores, no divergent loop.
-  uint32_t lu = excl >> 20, le = excl & 0xFFFFFu;
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
-    const int idx = lo + i * kLongNT + tid;
-    if (idx < n) {
-      const uint32_t b = bin_of(x[i]);
-      if (b > T) {
-        if (lu < (uint32_t)kKmax) s.chosen[lu] = idx;
-        ++lu;
-      } else if (b == T) {
-        if (le < (uint32_t)kLongCand) s.cand[le] = composite_key(x[i], idx);
-        ++le;
-      }
+  for (int p = 0; p < P; ++p) {
+    const uint32_t Bp = bin_pair(x[2 * p], x[2 * p + 1]);
+    uint32_t code;
+    if (lo + (2 * p + 2) * NT <= n) {  // the whole pair lies inside the row, for every lane
+      atomicAdd(&s.hist[Bp & 0xFFFFu], 1u);
+      atomicAdd(&s.hist[Bp >> 16], 1u);
+      code = Bp + 0x00010001u;
+    } else {
+      const bool ok0 = lo + entry_index<NT>(0, 2 * p) < n, ok1 = lo + entry_index<NT>(0, 2 * p + 1) < n;
+      if (ok0) atomicAdd(&s.hist[Bp & 0xFFFFu], 1u);
+      if (ok1) atomicAdd(&s.hist[Bp >> 16], 1u);
+      code = (ok0 ? (Bp & 0xFFFFu) + 1u : 0u) | (ok1 ? (Bp & 0xFFFF0000u) + 0x00010000u : 0u);
     }
-  }
-  if (tid == 0) {
-    s.base_up = bu;
-    s.base_cand = bc;
+    asm volatile("" : "+v"(code));
+    pb[p] = code;
   }
   __syncthreads();
-  const uint32_t tot_up = min(total >> 20, (uint32_t)kKmax), tot_eq = min(total & 0xFFFFFu, (uint32_t)kLongCand);
-  for (uint32_t j = tid; j < tot_up; j += kLongNT) {
-    const uint32_t pos = s.base_up + j;
-    if (pos < (uint32_t)m) {
-      const int idx = s.chosen[j];
-      out[pos] = idx;
-      if (TRANSLATE) {
-        if (tr.c == 1) translate_block_lds<1>(tr, r, (int)pos, idx, s.pages, first_lp);
-        else translate_block_lds<4>(tr, r, (int)pos, idx, s.pages, first_lp);
-      }
-    }
+  uint32_t hc[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) hc[i] = s.hist[kBins - 1 - B * tid - i];
+  uint32_t bq, aq, hq;
+  block_threshold<NT>(s, hc, q, bq, aq, hq);
+  uint32_t fl, cc;
+  if (aq + hq == (uint32_t)nck && nck <= Q) {
+    fl = 0;  // every entry kept
+    cc = (uint32_t)nck;
+  } else if (aq + hq <= (uint32_t)Q) {
+    fl = bq;
+    cc = aq + hq;
+  } else {
+    fl = bq + 1;
+    cc = aq;
   }
-  for (uint32_t j = tid; j < tot_eq; j += kLongNT) {
-    const uint32_t cpos = s.base_cand + j;
-    if (cpos < (uint32_t)kLongCand)
-      __hip_atomic_store(&gcand[cpos], s.cand[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Bit i: entry i is a candidate (code > fl, i.e. a bin >= fl inside the row).
+  const uint32_t tge = fl * 0x00010001u;
+  uint32_t gw = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const bs_ushort2 wt = {(uint16_t)(1u << (2 * p)), (uint16_t)(2u << (2 * p))};
+    gw = __builtin_amdgcn_udot2(__builtin_bit_cast(bs_ushort2, pk_gt_flags(pb[p], tge)), wt, gw, false);
   }
-  // Every lane's candidate stores have completed before the chunk arrives.
-  __builtin_amdgcn_s_waitcnt(0);
+  // Candidates go straight to this chunk's slots (one LDS atomic per wave
+  // hands out the positions), unused slots get the marker, and the histogram
+  // at and above the floor is published as 16-bit counts (this lane's two
+  // bins, adjacent, in one store).
+  // The stores are unconditional: a lane's non-candidate entries get an
+  // offset outside the buffer's range, which the hardware drops (no branch).
+  uint64_t* mine = gcand + (size_t)w * Q;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(mine, (short)0, Q * 8, 0x00020000);
+  uint32_t pos = wave_reserve_n(&s.emit, (uint32_t)__builtin_popcount(gw));
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const uint32_t on = (gw >> i) & 1u;
+    ws_buffer_store64(crs, on ? pos * 8u : 0x80000000u, (uint32_t)(lo + i * NT + tid), __float_as_uint(x[i]));
+    pos += on;
+  }
+  for (uint32_t j = cc + tid; j < (uint32_t)Q; j += NT) ws_store64(&mine[j], kNoCand);
+  {
+    const uint32_t b0 = (uint32_t)(kBins - 1 - 2 * tid);  // hc[0]; hc[1] is bin b0 - 1
+    const uint32_t pk = ((b0 >= fl ? hc[0] : 0u) << 16) | (b0 - 1 >= fl ? hc[1] : 0u);
+    ws_store32(reinterpret_cast<uint32_t*>(ghist) + (size_t)w * (kBins / 2) + (b0 - 1) / 2, pk);
+  }
+  if (tid == 0) ws_store32(&meta[w], (cc << 16) | fl);
+  __builtin_amdgcn_s_waitcnt(0);  // every store of this lane performed before the chunk arrives
   __syncthreads();
   if (tid == 0)
-    s.last = __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(nchunk - 1);
+    s.last = __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nchunk - 1);
   __syncthreads();
   if (!s.last) return;
 
-  // The last chunk to arrive resolves the boundary bin.  The head of the
-  // candidate list is read together with its length (one round trip); the
-  // list's storage holds kLongCand entries, those past the length are unused.
-  constexpr int kSpec = 4;
-  static_assert(kSpec * kLongNT <= kLongCand, "speculative reads stay inside the list");
-  uint64_t head[kSpec];
+  // ---- Resolution (the last chunk to arrive) ----
+  const int nall = nchunk * Q;
+  const bool fits = nall <= kCkAll && nchunk <= kCkMeta;
+  RowPagePrefetch<NT, TRANSLATE, kCkPages> pf{tr, r, gr};
+  uint64_t v[PA];
 #pragma unroll
-  for (int t = 0; t < kSpec; ++t)
-    head[t] = __hip_atomic_load(&gcand[t * kLongNT + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t nc = __hip_atomic_load(&ctr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t need = (uint32_t)m - above;
-  if (nc <= (uint32_t)kLongCand) {
+  for (int p = 0; p < PA; ++p) v[p] = kNoCand;
+  uint32_t mt = 0, hs[B];
 #pragma unroll
-    for (int t = 0; t < kSpec; ++t)
-      if ((uint32_t)(t * kLongNT + tid) < nc) s.cand[t * kLongNT + tid] = head[t];
-    for (int i = kSpec * kLongNT + tid; i < (int)nc; i += kLongNT)
-      s.cand[i] = __hip_atomic_load(&gcand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  bool translated = false;
-  if (need >= 1 && need <= (uint32_t)m) {
-    if (nc <= (uint32_t)kLongCand) {
-      if (need >= nc) {
-        for (uint32_t i = tid; i < nc; i += kLongNT) {
-          const uint32_t at = above + i;
-          if (at < (uint32_t)m) {
-            const int idx = index_of(s.cand[i]);
-            out[at] = idx;
-            s.chosen[at] = idx;
-          }
-        }
-      } else {
-        WinnerTr wt{};
-        if (TRANSLATE)
-          wt = WinnerTr{tr.page_table + (int64_t)g.b * tr.pt_stride, tr.c, g.nv, tr.pt_stride,
-                        tr.out_slots + (int64_t)r * tr.ld_out,
-                        tr.out_pos ? tr.out_pos + (int64_t)r * tr.ld_out : nullptr};
-        block_refine<kLongNT, kLongCand>(s, nc, need, out, s.chosen, above, m, wt);
-        translated = TRANSLATE;
+  for (int i = 0; i < B; ++i) hs[i] = 0;
+  if (fits) {
+    if (tid < nchunk) mt = ws_load32(&meta[tid]);
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      const int j = p * NT + tid;
+      v[p] = j < nall ? ws_load64(&gcand[j]) : kNoCand;
+    }
+    // The union's histogram: the sum of the chunks' published histograms
+    // (one packed load per chunk per lane), 32 chunks' loads in flight at a
+    // time (one round trip up to 32 chunks).
+    const uint32_t* gh32 = reinterpret_cast<const uint32_t*>(ghist);
+    for (int c0 = 0; c0 < nchunk; c0 += 32) {
+      uint32_t h[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        h[u] = c0 + u < nchunk ? ws_load32(&gh32[(size_t)(c0 + u) * (kBins / 2) + (kBins / 2 - 1 - tid)]) : 0u;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        hs[0] += h[u] >> 16;
+        hs[1] += h[u] & 0xFFFFu;
       }
-      __syncthreads();
-    } else {
-      if (tid == 0) s.emit = above;
-      __syncthreads();
-      block_refine_from_row<kLongNT, kLongCand>(s, row, n, T, need, out, s.chosen, m);
     }
   }
-  if (tid == 0) sel_count[r] = m;
-  if (TRANSLATE) {
-    if (!translated)
-      for (int q = (int)above + tid; q < m; q += kLongNT) translate_block(tr, g, r, q, s.chosen[q]);
-    translate_tail<kLongNT>(tr, g, r, m);
+  pf.issue();
+  if (fits && tid < nchunk) atomicMax(&s.bmax, mt & 0xFFFFu);
+  if (tid == 0) s.emit = 0;
+  pf.commit(s);
+  __syncthreads();
+  uint32_t T = 0, above = 0, inT = 0;
+  block_threshold<NT>(s, hs, (uint32_t)k, T, above, inT);
+  const bool fast = fits && T >= s.bmax;
+  if (fast) {
+    // Code per slot: bin + 1 for a candidate, 0 for an unused slot.
+    uint32_t code[PA];
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      const uint32_t b = bin_of(__uint_as_float((uint32_t)(v[p] >> 32))) + 1u;
+      code[p] = v[p] != kNoCand ? b : 0u;
+    }
+    // Above T: the selection (LDS); in T: the boundary list as composite
+    // keys.  Positions: one packed (above << 16 | in-bin) reservation per
+    // wave.  Every slot writes both lists, the ones it does not belong to at
+    // this lane's own scratch entries (no branch per slot).
+    const uint32_t t1 = T + 1u;
+    uint32_t upm = 0, eqm = 0;
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      upm |= (code[p] > t1 ? 1u : 0u) << p;
+      eqm |= (code[p] == t1 ? 1u : 0u) << p;
+    }
+    const uint32_t base =
+        wave_reserve_n(&s.emit, ((uint32_t)__builtin_popcount(upm) << 16) | (uint32_t)__builtin_popcount(eqm));
+    uint32_t pu = base >> 16, pe = base & 0xFFFFu;
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      const uint32_t up = (upm >> p) & 1u, eq = (eqm >> p) & 1u;
+      int32_t* du = up && pu < (uint32_t)k ? &s.chosen[pu] : &cs.trash32[tid];
+      uint64_t* de = eq && pe < (uint32_t)kCkCand ? &s.cand[pe] : &cs.trash64[tid];
+      *du = (int)(uint32_t)v[p];
+      *de = composite_key(__uint_as_float((uint32_t)(v[p] >> 32)), (int)(uint32_t)v[p]);
+      pu += up;
+      pe += eq;
+    }
+    __syncthreads();
+    const uint32_t nc = s.emit & 0xFFFFu, need = (uint32_t)k - above;
+    if (need >= 1 && need <= (uint32_t)k) {
+      if (nc <= (uint32_t)kCkCand) {
+        if (need >= nc) {
+          for (uint32_t i = tid; i < nc; i += NT) s.chosen[above + i] = index_of(s.cand[i]);
+        } else if (nc <= (uint32_t)kRankMax) {
+          rank_refine<NT>(s, nc, need, nullptr, s.chosen, above);
+        } else {
+          block_refine<NT>(s, nc, need, nullptr, s.chosen, above, k);
+        }
+        __syncthreads();
+      } else {
+        if (tid == 0) s.emit = above;
+        __syncthreads();
+        block_refine_from_row<NT>(s, row, n, T, need, nullptr, s.chosen, k);
+      }
+    }
+    for (int i = tid; i < k; i += NT) out[i] = s.chosen[i];
+    if (tid == 0) sel_count[r] = k;
+    if (TRANSLATE) translate_row<NT>(tr, pf.g, r, k, s.chosen, s.row_pages, (int)s.row_npages);
+  } else {
+    // Some chunk held more of the row's top than its quota: select the whole
+    // row here, streaming it (exact; rare on unclustered rows).
+    select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, k, k, out, sel_count, r, tr);
   }
-  // Leave the row's workspace zero-filled for the next call.
-  for (int i = tid; i < kBins; i += kLongNT) __hip_atomic_store(&gh[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (tid < 16) __hip_atomic_store(&ctr[tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int used = (int)min(nc, (uint32_t)kLongCand);
-  for (int i = tid; i < used; i += kLongNT)
-    __hip_atomic_store(&gcand[i], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) ws_store32(&ctr[0], 0u);
 }
 
-static bool use_long_path(int32_t num_rows, int32_t max_len) {
-  return max_len >= kLongMin && num_rows <= kLongRowsMax;
-}
+static bool use_long_path(int32_t max_len) { return max_len >= kLongMin; }
 
-size_t topk_workspace_size(int32_t num_rows, int32_t max_len, int32_t /*k*/) {
-  return use_long_path(num_rows, max_len) ? (size_t)num_rows * kWsRow : 0;
+size_t topk_workspace_size(int32_t num_rows, int32_t max_len, int32_t k) {
+  return use_long_path(max_len) ? (size_t)num_rows * ck_record_bytes(max_len, k) : 0;
 }
 
 template <bool TRANSLATE>
 static int launch_select(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows, int32_t max_len,
                          int32_t k, int32_t* sel, int32_t* sel_count, void* workspace, const Translate& tr,
                          hipStream_t stream) {
-  if (use_long_path(num_rows, max_len)) {
-    const int nchunk = (max_len + kChunk - 1) / kChunk;
-    const int nhist = (max_len + kHistChunk - 1) / kHistChunk;
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    hipLaunchKernelGGL(topk_long_hist_kernel<TRANSLATE>, dim3(num_rows, nhist), dim3(kLongNT), 0, stream, scores,
-                       ld, row_len, max_len, k, sel, sel_count, ws, tr);
-    if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
-    hipLaunchKernelGGL(topk_long_emit_kernel<TRANSLATE>, dim3(num_rows, nchunk), dim3(kLongNT), 0, stream, scores,
-                       ld, row_len, max_len, k, sel, sel_count, ws, tr);
+  if (use_long_path(max_len)) {
+    const int wmax = (max_len + kCkChunk - 1) / kCkChunk;
+    hipLaunchKernelGGL((topk_chunked_kernel<TRANSLATE, kCkNT>), dim3(num_rows, wmax), dim3(kCkNT), 0, stream, scores, ld,
+                       row_len, max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace),
+                       (int64_t)ck_record_bytes(max_len, k), wmax, tr);
   } else if (num_rows >= kManyMinRows && max_len <= kManyNT * kManyVpt) {
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kManyNT, kManyVpt, kManyCand>), dim3(num_rows), dim3(kManyNT), 0,
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
-  } else if (max_len > kRowNT * kRowVpt && max_len <= kMidNT * kMidVpt) {
+  } else if (max_len > kRowNT * kRowVpt) {
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kMidNT, kMidVpt, kMidCand>), dim3(num_rows), dim3(kMidNT), 0,
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   } else {

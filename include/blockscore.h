@@ -115,8 +115,9 @@ enum bs_status {
  * Returns BS_OK, BS_ERR_NULL (q, kcache, page_table, req_row_ptr, row_pos or
  * scores NULL with num_rows > 0), BS_ERR_ARG (c not 1 or 4, negative counts,
  * pt_stride < 1, num_pages < 1, max_vis < 0, ld_scores < max_vis,
- * c*max_vis > 64*pt_stride, num_req > 65535; idx_score_decode also
- * max_vis > 65535*4096, the selection's bound on a row) or BS_ERR_LAUNCH.
+ * c*max_vis > 64*pt_stride; idx_score_decode also num_req > 65535, one
+ * grid row per request, and max_vis > 65535*4096, the selection's bound on a
+ * row) or BS_ERR_LAUNCH.
  */
 int idx_score_decode(const uint16_t* q, const uint16_t* kcache, int64_t num_pages,
                      const int32_t* page_table, int32_t pt_stride,
@@ -143,9 +144,13 @@ int idx_score_prefill(const uint16_t* q, const uint16_t* kcache, int64_t num_pag
 
 /*
  * topk_workspace_bytes - device workspace topk_select_rows needs for
- * (num_rows, max_len, k).  0 means no workspace is needed (NULL may be
- * passed).  The workspace must be zero-filled before its first use; every call
- * leaves it zero-filled again, so one zero-fill at allocation suffices.
+ * (num_rows, max_len, k): num_rows records of a few KiB to a few hundred KiB
+ * when max_len >= 32,769 (rows that long are split over several workgroups),
+ * else 0, meaning no workspace is needed (NULL may be passed).  The workspace
+ * must be zero-filled before its first use; every call leaves it ready for
+ * the next one (its per-row arrival counters back at zero, the rest scratch
+ * that every call rewrites before reading), so one zero-fill at allocation
+ * suffices.
  */
 size_t topk_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k);
 
@@ -164,10 +169,15 @@ size_t topk_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k);
  * to an order-preserving 16-bit key whose upper 10 bits index a 1,024-bin
  * histogram; the bin holding the m-th largest is located, entries in higher
  * bins are emitted directly, and the boundary bin is resolved exactly on the
- * (FP32 key, index) pair by radix selection.  In a large batch each row is
- * done by one workgroup (in registers up to 32,768 entries, else streamed);
- * in a small batch (<= 256 rows) rows of >= 32,769 entries are split over
- * several workgroups whose histograms merge through device-scope atomics.
+ * (FP32 key, index) pair by radix selection.  A row of up to 32,768
+ * entries is done by one workgroup, in registers.  A longer row is split over
+ * one workgroup per 16,384 entries: each keeps the entries at or above the
+ * histogram bin of its local q-th largest (q a little above its share of the
+ * row's top k) as candidates and publishes them; the last to arrive builds
+ * the candidates' histogram, selects the threshold bin and resolves it, after
+ * checking that the candidates hold every entry of the row at or above that
+ * bin (when they do not, it selects the whole row itself).  The row's own
+ * length decides on the device; the host only bounds it by max_len.
  * Device preconditions: row_len[r] >= 0 (negative counts as 0); no NaN
  * (a NaN is ordered above +inf or below -inf by its sign bit).
  * Returns BS_OK, BS_ERR_NULL, BS_ERR_ARG (k outside 1..2048, max_len < 0,

@@ -84,6 +84,38 @@ def test_decode_many_rows_per_request(c):
     _full_check(inp)
 
 
+def _rows_per_request_batch(seed, c, rpr, k):
+    """Requests of exactly ``rpr`` query rows each (the row count per request
+    picks the decode kernel: 1-2 the VALU kernel with that many rows per pass,
+    3-4 the matrix-core kernel with 4 rows per pass).  Rows end at the last
+    context token; one request sits at the start of the context (n_vis = 0
+    for t <= 2 at c = 4) and one straddles a page boundary."""
+    rng = np.random.default_rng(seed)
+    ctx = [int(x) for x in rng.integers(200, 12000, 6)]
+    rows = [list(range(t - rpr, t)) for t in ctx]
+    ctx.append(rpr)
+    rows.append(list(range(rpr)))
+    b0 = 64 if c == 1 else 256  # first token of page 1 (c = 1) / block 64 (c = 4)
+    first = b0 - (rpr + 1) // 2
+    ctx.append(first + rpr + 1)
+    rows.append(list(range(first, first + rpr)))
+    return synth.build_paged_batch(f"rpr{rpr}", seed, c=c, k=k, ctx_tokens=ctx, row_pos_per_req=rows, rng=rng)
+
+
+@pytest.mark.parametrize("c", [4, 1])
+@pytest.mark.parametrize("rpr", [1, 2, 3, 4])
+def test_decode_each_rows_per_request_kernel(rpr, c):
+    inp = _rows_per_request_batch(500 + 10 * rpr + c, c, rpr, k=64)
+    assert np.all(np.diff(inp.req_row_ptr) == rpr)
+    _full_check(inp)
+
+
+def test_decode_verify_with_few_drafts():
+    # speculative verify with 1-3 draft tokens (2-4 rows per request)
+    for rows in (2, 3, 4):
+        _full_check(synth.qsa_verify_64req(B=12, verify_rows=rows, lo=300, hi=40000))
+
+
 def test_decode_power_of_two_scaling_exact():
     # s(2q) == 2*s(q) bit for bit in any fixed accumulation order.
     inp = synth.qsa_verify_64req(B=4, lo=1000, hi=9000)
@@ -163,10 +195,10 @@ def test_topk_mixed_lengths_one_launch():
 
 
 @pytest.mark.parametrize("R", [256, 257])
-def test_topk_long_row_count_boundary(R):
-    # Up to 256 rows of >= 32,769 entries split each row over many workgroups
-    # (workspace, device atomics); one more row and every row streams through
-    # one workgroup.  Odd k values, ragged lengths, tie storms.
+def test_topk_long_rows_many(R):
+    # Hundreds of rows of >= 32,769 entries, each split over chunk workgroups
+    # (workspace, device-scope hand-off), with a few short rows selected whole
+    # in the same launch.  Odd k values, ragged lengths, tie storms.
     n = 33000
     rng = np.random.default_rng(R)
     rows = rng.standard_normal((R, n)).astype(np.float32)
@@ -200,8 +232,7 @@ def test_topk_repeat_determinism_and_workspace_reset():
     ref_sel, ref_cnt = oracle.topk(w.scores, w.row_len, w.k)
     for sel, cnt in outs:
         check_topk_exact(sel, cnt, ref_sel, ref_cnt)
-    assert int(ws.count_nonzero().item()) == 0, "workspace must be left zero-filled"
-    # another batch through the same workspace
+    # another batch through the same workspace (left ready by the calls above)
     w2 = synth.topk_8x80k(seed=78)
     (out,), _ = gu.gpu_topk(w2.scores, w2.row_len, w2.k, workspace=ws)
     r2 = oracle.topk(w2.scores, w2.row_len, w2.k)
@@ -475,8 +506,149 @@ def test_fused_select_translate_on_given_rows():
         rs, rp, rc = oracle.expand_translate(inp, sel.cpu().numpy(), cnt.cpu().numpy())
         check_expand_exact(slots.cpu().numpy(), pos.cpu().numpy(), oc.cpu().numpy(), rs, rp, rc,
                            gu.pending_counts(inp))
-    if ws is not None:
-        assert int(ws.count_nonzero().item()) == 0
+
+
+def _given_rows_batch(rng, ctx, c, k, row_pos=None):
+    """A paged batch of one row per request (positions row_pos, default the
+    last context token) for selection on given FP32 rows: a seeded page
+    permutation, no keys (nothing is scored)."""
+    pages = [max(1, -(-t // 64)) for t in ctx]
+    perm = rng.permutation(int(sum(pages)))
+    pt = np.full((len(ctx), max(pages)), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        pt[b, :n] = perm[off:off + n]
+        off += n
+    t = np.array([x - 1 for x in ctx] if row_pos is None else row_pos, dtype=np.int32)
+    R = t.size
+    return synth.IndexerInputs(name="given", c=c, k=k, q=np.zeros((R, 4, 128), np.uint16),
+                               kcache=np.zeros((64 // c, 128), np.uint16), num_pages=int(off), page_table=pt,
+                               req_row_ptr=np.arange(R + 1, dtype=np.int32), row_pos=t,
+                               max_vis=int(((t.astype(np.int64) + 1) // c).max()), seed=0)
+
+
+def _select_translate_given(inp, rows, lens, max_len, reps=1):
+    """idx_select_translate on given FP32 rows; returns numpy outputs per rep."""
+    import torch
+    import block_scoring_top_amd as bst
+    from synth.device import upload
+    dev = upload(inp, "cuda")
+    R = inp.num_rows
+    s = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.float32)).cuda()
+    rl = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+    ws = bst.topk_workspace(R, max_len, inp.k, "cuda")
+    outs = []
+    for rep in range(reps):
+        gu.say(f"select_translate rows={R} max_len={max_len} k={inp.k} c={inp.c} rep={rep}")
+        sel = torch.full((R, inp.k), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+        slots = torch.full((R, inp.ld_out), -7, dtype=torch.int32, device="cuda")
+        pos = torch.full((R, inp.ld_out), -7, dtype=torch.int32, device="cuda")
+        oc = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+        bst.idx_select_translate(s, rl, max_len, inp.k, dev.req_row_ptr, dev.row_pos, inp.c, dev.page_table, sel,
+                                 cnt, slots, oc, out_pos=pos, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(tuple(t.cpu().numpy() for t in (sel, cnt, slots, pos, oc)))
+    return outs
+
+
+def _check_given(inp, rows, lens, outs):
+    ref_sel, ref_cnt = oracle.topk(np.ascontiguousarray(rows, dtype=np.float32), lens, inp.k)
+    for sel, cnt, slots, pos, oc in outs:
+        check_topk_exact(sel, cnt, ref_sel, ref_cnt)
+        rs, rp, rc = oracle.expand_translate(inp, sel, cnt)
+        check_expand_exact(slots, pos, oc, rs, rp, rc, gu.pending_counts(inp))
+
+
+@pytest.mark.parametrize("c", [4, 1])
+def test_fused_many_rows_exact(c):
+    # >= 1,024 rows of at most 16,384 entries: the many-rows shape of the fused
+    # kernel (256 lanes x 64 values, several rows per CU), bit-exact; tie
+    # storms, ragged lengths, rows whose boundary bin overflows the LDS list,
+    # and rows at positions past the 1,024 pages the kernel caches in LDS.
+    rng = np.random.default_rng(1200 + c)
+    R, n = 1040, 16384
+    k = 512 if c == 4 else 2048
+    ctx = [int(x) for x in rng.integers(2, 4 * n if c == 4 else n, R)]
+    ctx[:16] = [int(x) for x in rng.integers(70000, 90000, 16)]  # t/64 >= 1,024 pages
+    inp = _given_rows_batch(rng, ctx, c, k)
+    nv = (inp.row_pos.astype(np.int64) + 1) // c
+    lens = np.minimum(nv, n).astype(np.int32)
+    lens[16:20] = [0, 1, k, k + 1]
+    lens[16:20] = np.minimum(lens[16:20], nv[16:20])
+    rows = rng.standard_normal((R, n)).astype(np.float32)
+    rows[20:84] = synth.tie_storm_rows(1203, 64, n)
+    rows[84:100] = np.float32(1.0) + rng.integers(0, 3, (16, n)).astype(np.float32) * np.float32(2.0 ** -20)
+    assert inp.num_rows >= 1024 and int(lens.max()) <= n
+    _check_given(inp, rows, lens, _select_translate_given(inp, rows, lens, n))
+
+
+@pytest.mark.parametrize("c", [1, 4])
+def test_long_rows_fused_exact(c):
+    # rows of >= 32,769 entries (one workgroup per 16,384-entry chunk, the last
+    # to arrive resolving the row): random rows (candidate filter), tie storms
+    # and a row whose winners sit in one chunk (the whole-row fallback), row
+    # lengths that are not a multiple of the chunk, 3 calls on one workspace.
+    rng = np.random.default_rng(1300 + c)
+    k = 2048 if c == 1 else 512
+    lens = np.array([32769, 40000, 81920, 81920, 65537, 50001, 98304, 81920], dtype=np.int32)
+    ctx = [int(c * (n + 1)) for n in lens]
+    inp = _given_rows_batch(rng, ctx, c, k)
+    nv = (inp.row_pos.astype(np.int64) + 1) // c
+    assert np.all(nv >= lens)
+    ld = int(lens.max())
+    rows = rng.standard_normal((lens.size, ld)).astype(np.float32)
+    rows[1] = synth.tie_storm_rows(1301, 8, ld)[7]
+    rows[2] = synth.tie_storm_rows(1302, 8, ld)[1]
+    rows[3, 20000:23000] += np.float32(5.0)   # winners clustered in one chunk
+    rows[5] = np.abs(rows[5]) * np.float32(0.01)
+    _check_given(inp, rows, lens, _select_translate_given(inp, rows, lens, ld, reps=3))
+
+
+def test_long_rows_row_len_past_visible_blocks():
+    # row_len > n_vis on rows of >= 32,769 entries: chosen blocks at or past
+    # n_vis expand to -1 slots and positions (the -1 sentinel), the rest as
+    # usual, and the count is still c*m + p.
+    rng = np.random.default_rng(1400)
+    c, k = 4, 512
+    ctx = [90001, 140003, 70002]
+    inp = _given_rows_batch(rng, ctx, c, k, row_pos=[20000, 150, 70001])
+    nv = (inp.row_pos.astype(np.int64) + 1) // c
+    lens = np.array([40000, 33000, 34000], dtype=np.int32)
+    rows = rng.standard_normal((3, 40000)).astype(np.float32)
+    rows[0, 6000:] += np.float32(3.0)   # the top lies past n_vis = 5000
+    (sel, cnt, slots, pos, oc), = _select_translate_given(inp, rows, lens, 40000)
+    ref_sel, ref_cnt = oracle.topk(rows, lens, k)
+    check_topk_exact(sel, cnt, ref_sel, ref_cnt)
+    assert np.array_equal(oc, c * cnt + gu.pending_counts(inp))
+    for r in range(3):
+        m = int(cnt[r])
+        j = sel[r, :m].astype(np.int64)
+        ok = (j >= 0) & (j < nv[r])
+        want_pos = np.where(ok[:, None], c * j[:, None] + np.arange(c), -1)
+        page = inp.page_table[r, np.clip(c * j // 64, 0, inp.pt_stride - 1)]
+        want_slot = np.where(ok[:, None], page[:, None] * 64 + want_pos % 64, -1)
+        assert np.array_equal(pos[r, :c * m].reshape(m, c), want_pos)
+        assert np.array_equal(slots[r, :c * m].reshape(m, c), want_slot)
+        p = int(gu.pending_counts(inp)[r])
+        tail = c * int(nv[r]) + np.arange(p)
+        assert np.array_equal(pos[r, c * m:c * m + p], tail)
+        assert np.array_equal(slots[r, c * m:c * m + p], inp.page_table[r, tail // 64] * 64 + tail % 64)
+        assert np.all(slots[r, c * m + p:] == -1) and np.all(pos[r, c * m + p:] == -1)
+    assert (sel[0, :k] >= nv[0]).sum() > 100
+
+
+def test_mixed_batch_long_rows_among_many():
+    # 300 rows, 16 of them at 81,920 entries and the rest at 2,000-8,000: each
+    # long row is split over chunk workgroups and the others are selected whole,
+    # in one launch, whatever the row count.
+    rng = np.random.default_rng(1500)
+    R, c, k = 300, 1, 2048
+    lens = rng.integers(2000, 8001, R).astype(np.int32)
+    lens[rng.choice(R, 16, replace=False)] = 81920
+    inp = _given_rows_batch(rng, [int(n) for n in lens], c, k)
+    rows = rng.standard_normal((R, 81920)).astype(np.float32)
+    _check_given(inp, rows, lens, _select_translate_given(inp, rows, lens, 81920, reps=2))
 
 
 # ---------------------------------------------------------------------------
@@ -495,23 +667,11 @@ def test_prefill_multi_request_ragged():
     _full_check(inp, scorer="prefill")
 
 
-def test_prefill_full_size_sampled_rows():
-    # The full 8192-row prefill in the benchmark's launch shape; the oracle
-    # checks a sample of rows one by one.
-    inp = synth.qsa_prefill_8k()
-    g = gu.run_path(inp, "prefill")
-    rng = np.random.default_rng(3)
-    sample = np.sort(np.concatenate([[0, 1, 63, 64, 4095, 8191], rng.choice(8192, 40, replace=False)]))
-    sub = synth.IndexerInputs(**{**inp.__dict__, "q": inp.q[sample], "row_pos": inp.row_pos[sample],
-                                 "req_row_ptr": np.array([0, sample.size], dtype=np.int32)})
-    ref = oracle.pipeline(sub)
-    assert np.array_equal(g["row_len"][sample], ref["row_len"])
-    check_scores(g["scores"][sample], ref["scores"], ref["row_len"])
-    check_topk_e2e(g["sel"][sample], g["sel_count"][sample], ref["scores"], ref["sel"], ref["sel_count"],
-                   ref["row_len"])
-    slots, pos, oc = oracle.expand_translate(sub, g["sel"][sample], g["sel_count"][sample])
-    check_expand_exact(g["slots"][sample], g["pos"][sample], g["out_count"][sample], slots, pos, oc,
-                       gu.pending_counts(sub))
+def test_prefill_full_size_all_rows():
+    # The full 8,192-row prefill chunk in the benchmark's launch shape (the
+    # fused many-rows selection): every row's scores against the oracle, the
+    # exact top-k of the GPU's scores, the end-to-end band, the exact expansion.
+    _full_check(synth.qsa_prefill_8k(), scorer="prefill")
 
 
 def test_prefill_agrees_with_decode_scorer():
