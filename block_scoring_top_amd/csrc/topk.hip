@@ -882,11 +882,11 @@ struct RowPagePrefetch {
     g = row_geometry_finish(tr, r, gr);
     np = g.t >= 0 ? min((g.t >> 6) + 1, min(RP, tr.pt_stride)) : 0;
     const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
+    // Unconditional loads at clamped indices (a request's page-table row
+    // holds pt_stride >= 1 entries), masked in commit(): a conditional load
+    // would end in a wait at its branch join.
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = i * NT + (int)threadIdx.x;
-      v[i] = idx < np ? pt[idx] : -1;
-    }
+    for (int i = 0; i < PER; ++i) v[i] = pt[min(i * NT + (int)threadIdx.x, max(np - 1, 0))];
   }
   template <int CAP>
   __device__ __forceinline__ void commit(TopkShared<CAP, RP>& s) {
@@ -894,7 +894,7 @@ struct RowPagePrefetch {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int idx = i * NT + (int)threadIdx.x;
-      if (idx < RP) s.row_pages[idx] = v[i];
+      if (idx < RP) s.row_pages[idx] = idx < np ? v[i] : -1;
     }
     if (threadIdx.x == 0) s.row_npages = (uint32_t)np;
   }
@@ -981,6 +981,19 @@ __device__ __forceinline__ void ws_buffer_store64(__amdgpu_buffer_rsrc_t rs, uin
   constexpr int kSc1 = 16;
   __builtin_amdgcn_raw_buffer_store_b64(bs_u32x2{lo, hi}, rs, off, 0, kSc1);
 }
+// Loads through a buffer resource with the same cache policy (sc1): offsets
+// at or past the range return 0 without a memory access, so the loads are
+// unconditional (no branch, no wait at a join) and cost nothing where they
+// do not apply.
+__device__ __forceinline__ uint64_t ws_buffer_load64(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  constexpr int kSc1 = 16;
+  const bs_u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kSc1);
+  return ((uint64_t)v.y << 32) | v.x;
+}
+__device__ __forceinline__ uint32_t ws_buffer_load32(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  constexpr int kSc1 = 16;
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kSc1);
+}
 __device__ __forceinline__ uint32_t ws_load32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1035,13 +1048,11 @@ __global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
   for (int i = 0; i < VPT; ++i) x[i] = rdx.at(tid, lo + i * NT);
   const int n = max(0, min(row_len[r], max_len));
   int32_t* out = sel + (int64_t)r * k;
-  if (n < kLongMin) {
-    if (w == 0) select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, min(k, n), k, out, sel_count, r, tr);
-    return;
-  }
-  if (lo >= n) return;
+  // The branches on the row length come after the binning below, which
+  // consumes the loads above: left before it, they let the compiler sink
+  // the loads into the branch, after the length's round trip.
   const int nchunk = (n + CH - 1) / CH;
-  const int qn = ck_quota<CH>(n, k);
+  const int qn = ck_quota<CH>(max(n, kLongMin), k);  // used only when n >= kLongMin
   const int Q = ck_slots_for(qn);
   const int nck = min(CH, n - lo);
   const uint32_t q = (uint32_t)min(qn, nck);
@@ -1079,6 +1090,11 @@ __global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
     pb[p] = code;
   }
   __syncthreads();
+  if (n < kLongMin) {
+    if (w == 0) select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, min(k, n), k, out, sel_count, r, tr);
+    return;
+  }
+  if (lo >= n) return;
   uint32_t hc[B];
 #pragma unroll
   for (int i = 0; i < B; ++i) hc[i] = s.hist[kBins - 1 - B * tid - i];
@@ -1137,36 +1153,39 @@ __global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
   const bool fits = nall <= kCkAll && nchunk <= kCkMeta;
   RowPagePrefetch<NT, TRANSLATE, kCkPages> pf{tr, r, gr};
   uint64_t v[PA];
-#pragma unroll
-  for (int p = 0; p < PA; ++p) v[p] = kNoCand;
-  uint32_t mt = 0, hs[B];
+  uint32_t hs[B];
 #pragma unroll
   for (int i = 0; i < B; ++i) hs[i] = 0;
-  if (fits) {
-    if (tid < nchunk) mt = ws_load32(&meta[tid]);
+  // Every load below is unconditional, through buffer resources covering
+  // just the valid range (lanes past it read 0 without a memory access), and
+  // masked once it has arrived: a load under a condition ends in a wait at
+  // the branch join, which would serialise the round trips.
+  const uint32_t vmeta = fits ? (uint32_t)nchunk * 4u : 0u, vcand = fits ? (uint32_t)nall * 8u : 0u;
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(meta, (short)0, vmeta, 0x00020000);
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(gcand, (short)0, vcand, 0x00020000);
+  const __amdgpu_buffer_rsrc_t hrs =
+      __builtin_amdgcn_make_buffer_rsrc(ghist, (short)0, fits ? (uint32_t)nchunk * kBins * 2u : 0u, 0x00020000);
+  const uint32_t mt = ws_buffer_load32(mrs, (uint32_t)tid * 4u);
 #pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      const int j = p * NT + tid;
-      v[p] = j < nall ? ws_load64(&gcand[j]) : kNoCand;
-    }
-    // The union's histogram: the sum of the chunks' published histograms
-    // (one packed load per chunk per lane), 32 chunks' loads in flight at a
-    // time (one round trip up to 32 chunks).
-    const uint32_t* gh32 = reinterpret_cast<const uint32_t*>(ghist);
-    for (int c0 = 0; c0 < nchunk; c0 += 32) {
-      uint32_t h[32];
+  for (int p = 0; p < PA; ++p) v[p] = ws_buffer_load64(grs, (uint32_t)(p * NT + tid) * 8u);
+  // The union's histogram: the sum of the chunks' published histograms
+  // (one packed load per chunk per lane), 32 chunks' loads in flight at a
+  // time (one round trip up to 32 chunks).
+  for (int c0 = 0; c0 < (fits ? nchunk : 0); c0 += 32) {
+    uint32_t h[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        h[u] = c0 + u < nchunk ? ws_load32(&gh32[(size_t)(c0 + u) * (kBins / 2) + (kBins / 2 - 1 - tid)]) : 0u;
+    for (int u = 0; u < 32; ++u)
+      h[u] = ws_buffer_load32(hrs, ((uint32_t)(c0 + u) * (kBins / 2) + (uint32_t)(kBins / 2 - 1 - tid)) * 4u);
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        hs[0] += h[u] >> 16;
-        hs[1] += h[u] & 0xFFFFu;
-      }
+    for (int u = 0; u < 32; ++u) {
+      hs[0] += h[u] >> 16;
+      hs[1] += h[u] & 0xFFFFu;
     }
   }
+#pragma unroll
+  for (int p = 0; p < PA; ++p) v[p] = p * NT + tid < nall ? v[p] : kNoCand;
   pf.issue();
-  if (fits && tid < nchunk) atomicMax(&s.bmax, mt & 0xFFFFu);
+  if (tid < nchunk) atomicMax(&s.bmax, mt & 0xFFFFu);
   if (tid == 0) s.emit = 0;
   pf.commit(s);
   __syncthreads();
