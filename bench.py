@@ -8,11 +8,17 @@ the uncompressed (c = 1) DSA-style decode: 16 requests x 1 row at L = 81,920
 tokens, an independent 81,920 x 128 bf16 key set per request (320 MiB),
 top-2048, translation through 64-token pages.
 
-Prints one JSON line.  `value` is rows/s over the timed steps; `roofline`
-covers the dominant kernel (the decode scorer, HBM bound) with its average
-launch time taken from HIP events recorded around each launch on the stream
-it runs on; `cpu_baseline` is the CPU oracle timed on the host on repeated
-full batches of the same workload.
+Prints one JSON line.  `value` is rows/s over the timed steps (two HIP
+events around K steps).  `roofline` covers the dominant kernel (the decode
+scorer, HBM bound): its average launch duration comes from HIP events on its
+stream around back-to-back launches right after the timed region (the figure
+a kernel trace reports), its bytes count its own output (the scores); the
+committed kernel trace's average and the fraction it gives are reported
+beside it when the trace was taken on the current source.  `step_roofline`
+is the whole step against HBM peak, counting the algorithmic bytes of the
+path (keys once, q, page-table entries, the selection; scores are an
+intermediate).  `cpu_baseline` is the CPU oracle timed on the host on
+repeated full batches of the same workload.
 """
 from __future__ import annotations
 
@@ -96,33 +102,50 @@ def cpu_baseline(inp, min_seconds: float):
         if el >= min_seconds or reps >= 5000:
             break
     what = "top-k (full sort)" if topk_only else "score + top-k (full sort) + expand/translate"
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(inp.num_rows * reps / el, 2), "unit": "rows/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{reps} full batches of the timed workload ({inp.num_rows} rows each) through {what}, "
                       f"{el:.1f} s"}
 
 
-def time_steps(fns, K, warmup, stream, probe=0, probe_every=10):
+def time_steps(fns, K, warmup, stream, probe=0, probe_every=10, burst=20):
     """Runs the callables of a step K times after `warmup` untimed steps and
-    returns (ms per step, avg ms of fns[probe]).
+    returns (ms per step, dict of dominant-kernel timings).
 
-    The step time comes from two HIP events around all K steps.  fns[probe]
-    (the dominant kernel) is bracketed by its own pair of HIP events on every
-    `probe_every`-th step of the same timed region; every event is recorded on
-    `stream`, the stream all calls are launched on.  (An event marker costs the
-    GPU a few microseconds, so bracketing every kernel of every step would
-    inflate the step time.)"""
+    The step time comes from two HIP events around the K steps, with nothing
+    else recorded in between.  The dominant callable fns[probe] is then timed
+    twice, every event recorded on `stream`, the stream all calls are
+    launched on:
+      * burst_ms: events around `burst` back-to-back launches of it alone,
+        divided by `burst` -- its average launch duration, the figure a
+        kernel trace reports (the launches queue behind each other, so the
+        dispatch latency is paid once);
+      * in_steps_ms: events around it inside `probe_every`-th steps of a
+        second run of K steps (each bracket also holds the launch latency of
+        a kernel queued behind an event marker, a few microseconds)."""
     import numpy as np
     import torch
     for _ in range(warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
-    probes = []
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
+    for _ in range(K):
+        for f in fns:
+            f()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    probes = []
     for i in range(K):
         for j, f in enumerate(fns):
             if j == probe and i % probe_every == 0:
@@ -133,10 +156,72 @@ def time_steps(fns, K, warmup, stream, probe=0, probe_every=10):
                 probes.append((a, b))
             else:
                 f()
-    end.record(stream)
     torch.cuda.synchronize()
-    t_probe = float(np.mean([a.elapsed_time(b) for a, b in probes]))
-    return start.elapsed_time(end) / K, t_probe
+    in_steps = float(np.mean([a.elapsed_time(b) for a, b in probes]))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(burst):
+        fns[probe]()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return ms, {"burst_ms": a.elapsed_time(b) / burst, "in_steps_ms": in_steps, "burst": burst}
+
+
+def cold_steps(fns, reps, stream, flush_bytes=512 << 20):
+    """Median step time with the 256 MB Infinity Cache flushed before every
+    step: a `flush_bytes` scratch buffer is written between steps, outside
+    the events that bracket each step."""
+    import numpy as np
+    import torch
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device=torch.cuda.current_device())
+    times = []
+    for i in range(reps):
+        scratch.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for f in fns:
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del scratch
+    return float(np.median(times))
+
+
+def kernel_trace_us(kernel_key: str, digest: str):
+    """Average duration (us) of a kernel in the committed rocprofv3 kernel
+    trace of this workload, if that trace was taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "kernel_trace.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel_key)
+    if not ent or ent.get("source_digest") != digest:
+        return None
+    return ent.get("avg_us")
+
+
+def step_bytes(inp) -> int:
+    """Algorithmic HBM bytes of one pass of the whole path (score -> top-k ->
+    expand/translate): each request's visible keys once (256 B), each row's q
+    (1 KiB), the page-table entries of the visible range (4 B), and the
+    selection written (k int32 per row).  Scores are an intermediate (written
+    by the scorer, read by the selection) and are not counted; neither are
+    the translated slots and positions (8 B per expanded entry), reported
+    separately."""
+    import numpy as np
+    per_page = 64 // inp.c
+    keys = pages = 0
+    for b in range(inp.num_req):
+        rows = inp.row_pos[inp.req_row_ptr[b]:inp.req_row_ptr[b + 1]]
+        if rows.size == 0:
+            continue
+        nmax = int(((rows.astype(np.int64) + 1) // inp.c).max())
+        keys += nmax
+        pages += -(-nmax // per_page)
+    return int(keys * 256 + inp.num_rows * 1024 + pages * 4 + inp.num_rows * inp.k * 4)
 
 
 def kernel_breakdown(fns, K, stream):
@@ -156,7 +241,7 @@ def kernel_breakdown(fns, K, stream):
     return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(len(fns))]
 
 
-def run_workload(name, K, warmup, dev, fused=True):
+def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
     import torch
 
     import block_scoring_top_amd as bst
@@ -174,7 +259,8 @@ def run_workload(name, K, warmup, dev, fused=True):
         sel = torch.empty((inp.num_rows, inp.k), dtype=torch.int32, device=dev)
         cnt = torch.empty(inp.num_rows, dtype=torch.int32, device=dev)
         ws = bst.topk_workspace(inp.num_rows, inp.max_len, inp.k, dev)
-        ms, t_topk = time_steps([bst.prepare_topk(s, rl, inp.max_len, inp.k, sel, cnt, ws)], K, warmup, stream)
+        ms, kt = time_steps([bst.prepare_topk(s, rl, inp.max_len, inp.k, sel, cnt, ws)], K, warmup, stream)
+        t_topk = kt["burst_ms"]
         alg = inp.num_rows * inp.max_len * 4 + inp.num_rows * inp.k * 4
         ach = alg / (t_topk * 1e-3) / 1e9
         log(f"{name}: {ms * 1e3:.1f} us/step (top-k {t_topk * 1e3:.1f} us)")
@@ -195,33 +281,59 @@ def run_workload(name, K, warmup, dev, fused=True):
         fns, names = list(path.prepared()), ["score", "select_translate"]
     else:
         fns, names = [path.score, path.select, path.expand], ["score", "topk", "expand"]
-    ms, t_score = time_steps(fns, K, warmup, stream, probe=0)
+    ms, kt = time_steps(fns, K, warmup, stream, probe=0)
+    t_score = kt["burst_ms"]
     br = kernel_breakdown(fns, K, stream)
-    log(f"{name}: {ms * 1e3:.1f} us/step; score {t_score * 1e3:.1f} us (timed region); separate pass: " +
-        ", ".join(f"{n} {t * 1e3:.1f} us" for n, t in zip(names, br)))
+    cold = cold_steps(fns, 20, stream) if cold_reps else None
+    log(f"{name}: {ms * 1e3:.1f} us/step; score {t_score * 1e3:.1f} us ({kt['burst']} back-to-back), "
+        f"{kt['in_steps_ms'] * 1e3:.1f} us inside steps; separate pass: " +
+        ", ".join(f"{n} {t * 1e3:.1f} us" for n, t in zip(names, br)) +
+        (f"; cold (Infinity Cache flushed) {cold * 1e3:.1f} us/step" if cold else ""))
+    method = (f"HIP events on the launch stream around {kt['burst']} back-to-back launches, right after the "
+              "timed region")
     if scorer == "decode":
+        kname, dig = "score_decode_kernel", source_digest("score_decode.hip", "device.h")
         alg = scorer_bytes(inp)
         ach = alg / (t_score * 1e-3) / 1e9
+        tr = kernel_trace_us(f"{name}:{kname}", dig)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("score_decode", source_digest("score_decode.hip", "device.h")),
-                "kernel": "score_decode_kernel", "algorithmic_bytes": alg, "avg_us": round(t_score * 1e3, 2)}
+                "traffic": measured_traffic("score_decode", dig),
+                "kernel": kname, "algorithmic_bytes": alg, "avg_us": round(t_score * 1e3, 2), "avg_us_method": method,
+                "avg_us_in_steps": round(kt["in_steps_ms"] * 1e3, 2),
+                "kernel_trace_avg_us": tr,
+                "frac_kernel_trace": round(alg / (tr * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if tr else None}
     else:
+        kname, dig = "score_prefill_kernel", source_digest("score_prefill.hip", "device.h")
         fl = prefill_flops(inp)
         ach = fl / (t_score * 1e-3) / 1e12
+        tr = kernel_trace_us(f"{name}:{kname}", dig)
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("score_prefill", source_digest("score_prefill.hip", "device.h")),
-                "kernel": "score_prefill_kernel", "algorithmic_flops": fl, "avg_us": round(t_score * 1e3, 2)}
-    return {"_inp": inp, "rows_per_s": round(inp.num_rows / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
-            "config": {"workload": name, "rows": inp.num_rows, "requests": inp.num_req,
-                       "max_visible_blocks": inp.max_vis, "k": inp.k, "c": inp.c, "scorer": scorer,
-                       "page_tokens": 64,
-                       "steps": "score -> select+translate (one kernel)" if fused else
-                                "score -> top-k -> expand/translate"},
-            "kernels_us": {**{n: round(t * 1e3, 2) for n, t in zip(names, br)},
-                           "note": "separate pass after the timed region, every call bracketed by HIP events"},
-            "roofline": roof}
+                "traffic": measured_traffic("score_prefill", dig),
+                "kernel": kname, "algorithmic_flops": fl, "avg_us": round(t_score * 1e3, 2), "avg_us_method": method,
+                "avg_us_in_steps": round(kt["in_steps_ms"] * 1e3, 2),
+                "kernel_trace_avg_us": tr,
+                "frac_kernel_trace": round(fl / (tr * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4) if tr else None}
+    sb = step_bytes(inp)
+    step_roof = {"bound": "hbm", "algorithmic_bytes": sb, "achieved": round(sb / (ms * 1e-3) / 1e9, 1),
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "bytes": "keys once per request + q + page-table entries + selection written; scores are an "
+                          "intermediate, not counted"}
+    out = {"_inp": inp, "rows_per_s": round(inp.num_rows / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+           "config": {"workload": name, "rows": inp.num_rows, "requests": inp.num_req,
+                      "max_visible_blocks": inp.max_vis, "k": inp.k, "c": inp.c, "scorer": scorer,
+                      "page_tokens": 64,
+                      "steps": "score -> select+translate (one kernel)" if fused else
+                               "score -> top-k -> expand/translate"},
+           "kernels_us": {**{n: round(t * 1e3, 2) for n, t in zip(names, br)},
+                          "note": "separate pass after the timed region, every call bracketed by HIP events"},
+           "roofline": roof, "step_roofline": step_roof}
+    if cold:
+        out["cold_ms_per_step"] = round(cold, 5)
+        out["cold_note"] = ("median of 20 steps, each after writing a 512 MiB scratch buffer (flushes the 256 MB "
+                            "Infinity Cache), outside the events")
+    return out
 
 
 def run_indexshare(name, inp, K, warmup, dev, stream):
@@ -248,7 +360,8 @@ def run_indexshare(name, inp, K, warmup, dev, stream):
     cnt = torch.empty(R, dtype=torch.int32, device=dev)
     call = bst.prepare_expand_shared(path.sel, path.sel_count, d.k, d.req_row_ptr, d.row_pos, now, d.c, adv,
                                      d.page_table, slots, cnt, out_pos=pos)
-    ms, t_call = time_steps([call], K, warmup, stream)
+    ms, kt = time_steps([call], K, warmup, stream)
+    t_call = kt["burst_ms"]
     torch.cuda.synchronize()
     n_out = int(cnt.sum().item())
     alg = int(path.sel_count.sum().item()) * 4 + n_out * (4 + 4) + R * 16  # selection in, slots + positions out
@@ -274,7 +387,8 @@ def run_compress(name, ci, K, warmup, dev, stream):
 
     d = upload_compress(ci, dev)
     call = bst.prepare_compress_store(*d.args())
-    ms, t_call = time_steps([call], K, warmup, stream)
+    ms, kt = time_steps([call], K, warmup, stream)
+    t_call = kt["burst_ms"]
     counts = np.diff(ci.req_tok_ptr).astype(np.int64)
     starts = ci.tok_start.astype(np.int64)
     blocks = (starts + counts) // 4 - starts // 4
@@ -308,6 +422,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every other workload (extra field)")
     ap.add_argument("--unfused", action="store_true", help="separate top-k and expand calls")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps with the Infinity Cache flushed before each (always on with --all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -334,14 +450,14 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
         return
-    res = run_workload(args.workload, args.steps, args.warmup, dev, fused=not args.unfused)
+    res = run_workload(args.workload, args.steps, args.warmup, dev, fused=not args.unfused, cold_reps=args.cold)
     inp = res.pop("_inp")
     extra = {}
     if args.all:
         for name in synth.WORKLOADS:
             if name == args.workload:
                 continue
-            r = run_workload(name, args.steps, args.warmup, dev, fused=not args.unfused)
+            r = run_workload(name, args.steps, args.warmup, dev, fused=not args.unfused, cold_reps=True)
             r.pop("_inp")
             extra[name] = r
     cpu = None
@@ -365,8 +481,12 @@ def main():
         "config": res["config"],
         "kernels_us": res["kernels_us"],
         "roofline": res["roofline"],
+        "step_roofline": res.get("step_roofline"),
         "cpu_baseline": cpu,
     }
+    for key in ("cold_ms_per_step", "cold_note"):
+        if key in res:
+            line[key] = res[key]
     if extra:
         line["other_workloads"] = extra
     print(json.dumps(line), flush=True)
