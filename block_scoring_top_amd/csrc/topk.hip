@@ -107,10 +107,14 @@ __host__ __device__ constexpr size_t ck_hist_offset(int wmax) { return kWsMeta +
 __host__ __device__ constexpr size_t ck_cand_offset(int wmax) {
   return ck_hist_offset(wmax) + (size_t)wmax * kBins * 2;
 }
+// Records are whole blocks of kWsBlock bytes, so every row counter of every
+// layout sits on the first word of such a block: a call that leaves those
+// words zero leaves the workspace ready for any later shape.
+constexpr size_t kWsBlock = (size_t)64 << 10;
 static size_t ck_record_bytes(int32_t max_len, int32_t k) {
   const int wmax = (max_len + kCkChunk - 1) / kCkChunk;
   const size_t b = ck_cand_offset(wmax) + (size_t)wmax * ck_slots<kCkChunk>(kLongMin, k) * 8;
-  return (b + 255) / 256 * 256;
+  return (b + kWsBlock - 1) / kWsBlock * kWsBlock;
 }
 
 template <int CAP, int RP = kRowPages>
@@ -1250,7 +1254,12 @@ __global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
     // row here, streaming it (exact; rare on unclustered rows).
     select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, k, k, out, sel_count, r, tr);
   }
-  if (tid == 0) ws_store32(&ctr[0], 0u);
+  // Leave the first word of every kWsBlock-byte block of the row's record
+  // zero: every layout a later call may lay over the workspace (other row
+  // counts, lengths, k) puts its row counters on such words, and everything
+  // else a call reads it has written first.
+  for (int i = tid; i < (int)(rec_bytes / kWsBlock); i += NT)
+    ws_store32(reinterpret_cast<uint32_t*>(rec + (size_t)i * kWsBlock), 0u);
 }
 
 static bool use_long_path(int32_t max_len) { return max_len >= kLongMin; }

@@ -144,13 +144,15 @@ int idx_score_prefill(const uint16_t* q, const uint16_t* kcache, int64_t num_pag
 
 /*
  * topk_workspace_bytes - device workspace topk_select_rows needs for
- * (num_rows, max_len, k): num_rows records of a few KiB to a few hundred KiB
- * when max_len >= 32,769 (rows that long are split over several workgroups),
- * else 0, meaning no workspace is needed (NULL may be passed).  The workspace
- * must be zero-filled before its first use; every call leaves it ready for
- * the next one (its per-row arrival counters back at zero, the rest scratch
- * that every call rewrites before reading), so one zero-fill at allocation
- * suffices.
+ * (num_rows, max_len, k): num_rows records of 64 KiB blocks (128 KiB per row
+ * at max_len = 81,920) when max_len >= 32,769 (rows that long are split over
+ * several workgroups), else 0, meaning no workspace is needed (NULL may be
+ * passed).  The workspace must be zero-filled before its first use.  Every
+ * call leaves the first 4 bytes of every 64 KiB block of it zero again, which
+ * is all that a later call relies on (its per-row counters sit there;
+ * everything else it reads it writes first), so one zero-fill at allocation
+ * suffices, also when later calls use other shapes that fit it.  The rest of
+ * its contents between calls is unspecified.
  */
 size_t topk_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k);
 

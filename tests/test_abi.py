@@ -222,3 +222,4 @@ def test_compress_validation():
     for k in ("k_raw", "ptr", "start", "ring", "pt", "kc"):
         assert _compress(**{k: NULL}) == BS_ERR_NULL, k
     assert _compress(mpos=FAKE) == BS_ERR_NULL              # MRoPE positions need ring_pos
+

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import synth
@@ -135,6 +136,12 @@ def test_decode_leaves_invisible_entries_untouched():
         assert np.all(np.isnan(s[r, rl[r]:]))
 
 
+def _ws_clean(ws) -> bool:
+    """What every call must leave in a workspace for the next: the first
+    4 bytes of every 64 KiB block zero."""
+    return int(ws.view(torch.int32)[::16384].count_nonzero().item()) == 0 if ws is not None else True
+
+
 # ---------------------------------------------------------------------------
 # Top-k on given FP32 rows: bit-exact
 # ---------------------------------------------------------------------------
@@ -232,11 +239,30 @@ def test_topk_repeat_determinism_and_workspace_reset():
     ref_sel, ref_cnt = oracle.topk(w.scores, w.row_len, w.k)
     for sel, cnt in outs:
         check_topk_exact(sel, cnt, ref_sel, ref_cnt)
-    # another batch through the same workspace (left ready by the calls above)
+    assert _ws_clean(ws), "the first word of every 64 KiB block of the workspace must be left zero"
+    # another batch through the same workspace
     w2 = synth.topk_8x80k(seed=78)
     (out,), _ = gu.gpu_topk(w2.scores, w2.row_len, w2.k, workspace=ws)
     r2 = oracle.topk(w2.scores, w2.row_len, w2.k)
     check_topk_exact(out[0], out[1], *r2)
+
+
+def test_topk_workspace_reused_across_shapes():
+    # One zero-filled workspace, sized for the largest call, used by calls of
+    # other row counts, lengths and k in turn: each leaves it zero-filled, so
+    # the next call's layout over it starts from zeros.
+    rng = np.random.default_rng(2024)
+    shapes = [(16, 81920, 2048), (3, 50000, 512), (40, 33000, 100), (16, 81920, 2048), (7, 70000, 2047)]
+    import block_scoring_top_amd as bst
+    big = max(bst.topk_workspace_bytes(R, n, k) for R, n, k in shapes)
+    import torch
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    for R, n, k in shapes:
+        rows = rng.standard_normal((R, n)).astype(np.float32)
+        lens = rng.integers(32769, n + 1, R).astype(np.int32)
+        (out,), _ = gu.gpu_topk(rows, lens, k, workspace=ws)
+        check_topk_exact(out[0], out[1], *oracle.topk(rows, lens, k))
+        assert _ws_clean(ws)
 
 
 def test_topk_qsa_score_rows():
@@ -549,6 +575,8 @@ def _select_translate_given(inp, rows, lens, max_len, reps=1):
                                  cnt, slots, oc, out_pos=pos, workspace=ws)
         torch.cuda.synchronize()
         outs.append(tuple(t.cpu().numpy() for t in (sel, cnt, slots, pos, oc)))
+        if ws is not None:
+            assert _ws_clean(ws), "the first word of every 64 KiB block of the workspace must be left zero"
     return outs
 
 
