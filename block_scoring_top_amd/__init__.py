@@ -27,6 +27,7 @@ HEADS = 4
 DIM = 128
 PAGE_TOKENS = 64
 KMAX = 2048
+NOALLOC_SCRATCH_BYTES = 8 << 20  # BS_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -61,6 +62,9 @@ def lib():
         L.idx_select_translate.argtypes = [P, i64, P, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P, P, i32,
                                            P, C.c_size_t, P]
         L.idx_select_translate.restype = C.c_int
+        L.idx_select_translate_noalloc.argtypes = [P, i64, P, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P, P,
+                                                   i32, P]
+        L.idx_select_translate_noalloc.restype = C.c_int
         L.idx_compress_store.argtypes = [P, i32, P, P, P, i32, i32, i32, i32, i32, i32, C.c_double, P, P, P, i32,
                                          P, i64, P]
         L.idx_compress_store.restype = C.c_int
@@ -261,6 +265,16 @@ def idx_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, c, p
     _check(lib().idx_select_translate(*args, _stream(stream, scores.device)), "idx_select_translate")
 
 
+def idx_select_translate_noalloc(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                                 out_slots, out_count, out_pos=None, stream=None):
+    """``idx_select_translate`` without a workspace (static device scratch of
+    NOALLOC_SCRATCH_BYTES per GPU).  See ``idx_select_translate_noalloc`` in
+    blockscore.h."""
+    args = _select_translate_args(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel,
+                                  sel_count, out_slots, out_count, out_pos, None)[:-2]
+    _check(lib().idx_select_translate_noalloc(*args, _stream(stream, scores.device)), "idx_select_translate_noalloc")
+
+
 def _compress_args(k_raw, req_tok_ptr, tok_start, mrope_pos, max_tok, rotary_dim, sections, theta, ring,
                    ring_pos, page_table, kcache, num_pages):
     """Checked argument tuple of an ``idx_compress_store`` call (all but the stream)."""
@@ -348,7 +362,7 @@ def prepare_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, 
 __all__ = [
     "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
     "topk_select_rows", "idx_expand_translate", "idx_expand_translate_shared", "idx_select_translate",
-    "idx_compress_store", "status_string", "BlockScoreError",
+    "idx_select_translate_noalloc", "NOALLOC_SCRATCH_BYTES", "idx_compress_store", "status_string", "BlockScoreError",
     "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate", "prepare_expand_shared",
     "prepare_compress_store",
 ]

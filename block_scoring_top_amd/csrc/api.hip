@@ -7,6 +7,8 @@
 #include "../../include/blockscore.h"
 #include "kernels.h"
 
+static_assert(BS_NOALLOC_SCRATCH_BYTES == bs::kNoAllocScratchBytes, "the header states the scratch size");
+
 #define BS_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -141,6 +143,29 @@ BS_EXPORT int idx_select_translate(const float* scores, int64_t ld_scores, const
                                      out_count, ld_out, workspace, static_cast<hipStream_t>(stream));
 }
 
+BS_EXPORT int idx_select_translate_noalloc(const float* scores, int64_t ld_scores, const int32_t* row_len,
+                                           int32_t num_rows, int32_t max_len, int32_t k,
+                                           const int32_t* req_row_ptr, int32_t num_req, const int32_t* row_pos,
+                                           int32_t c, const int32_t* page_table, int32_t pt_stride,
+                                           int32_t* sel, int32_t* sel_count,
+                                           int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
+                                           void* stream) {
+  if (num_rows < 0 || num_req < 0 || max_len < 0 || k < 1 || k > BS_KMAX) return BS_ERR_ARG;
+  if (c != 1 && c != 4) return BS_ERR_ARG;
+  if ((int64_t)ld_out < (int64_t)k * c + c - 1) return BS_ERR_ARG;
+  if (num_rows == 0) return BS_OK;
+  if (num_req == 0) return BS_ERR_ARG;
+  if (!scores || !row_len || !sel || !sel_count || !req_row_ptr || !row_pos || !page_table || !out_slots ||
+      !out_count)
+    return BS_ERR_NULL;
+  if (ld_scores < (int64_t)max_len || pt_stride < 1) return BS_ERR_ARG;
+  if ((int64_t)max_len > (int64_t)65535 * 4096) return BS_ERR_ARG;  // grid y limit
+  if (bs::topk_workspace_size(num_rows, max_len, k) > BS_NOALLOC_SCRATCH_BYTES) return BS_ERR_WORKSPACE;
+  return bs::launch_select_translate_noalloc(scores, ld_scores, row_len, num_rows, max_len, k, req_row_ptr, num_req,
+                                             row_pos, c, page_table, pt_stride, sel, sel_count, out_slots, out_pos,
+                                             out_count, ld_out, static_cast<hipStream_t>(stream));
+}
+
 BS_EXPORT int idx_compress_store(const uint16_t* k_raw, int32_t num_tok, const int32_t* req_tok_ptr,
                                  const int32_t* tok_start, const int32_t* mrope_pos, int32_t num_req,
                                  int32_t max_tok, int32_t rotary_dim, int32_t sec_t, int32_t sec_h, int32_t sec_w,
@@ -165,7 +190,9 @@ BS_EXPORT const char* bs_status_string(int status) {
     case BS_OK: return "BS_OK";
     case BS_ERR_NULL: return "BS_ERR_NULL: a required pointer is NULL";
     case BS_ERR_ARG: return "BS_ERR_ARG: a size, stride, k or c is out of range";
-    case BS_ERR_WORKSPACE: return "BS_ERR_WORKSPACE: workspace missing or too small";
+    case BS_ERR_WORKSPACE:
+      return "BS_ERR_WORKSPACE: workspace missing or too small (idx_select_translate_noalloc: the call needs more "
+             "than its static scratch of BS_NOALLOC_SCRATCH_BYTES)";
     case BS_ERR_LAUNCH: return "BS_ERR_LAUNCH: the HIP runtime rejected a launch";
     default: return "unknown status";
   }

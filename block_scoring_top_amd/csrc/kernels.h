@@ -33,6 +33,15 @@ int launch_select_translate(const float* scores, int64_t ld, const int32_t* row_
                             int32_t* sel, int32_t* sel_count, int32_t* out_slots, int32_t* out_pos,
                             int32_t* out_count, int32_t ld_out, void* workspace, hipStream_t stream);
 
+// The same with the long-row records in a static device array of
+// kNoAllocScratchBytes (per GPU); the caller checks the size first.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+int launch_select_translate_noalloc(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows,
+                                    int32_t max_len, int32_t k, const int32_t* req_row_ptr, int32_t num_req,
+                                    const int32_t* row_pos, int32_t c, const int32_t* page_table, int32_t pt_stride,
+                                    int32_t* sel, int32_t* sel_count, int32_t* out_slots, int32_t* out_pos,
+                                    int32_t* out_count, int32_t ld_out, hipStream_t stream);
+
 // row_pos_now == nullptr: the plain expansion; otherwise the IndexShare one
 // (tail through row_pos_now[r], at most max_advance past row_pos[r]).
 int launch_expand(const int32_t* sel, const int32_t* sel_count, int32_t k,

@@ -43,6 +43,8 @@
 //   * emission is count, block scan, write (no per-entry atomics); the
 //     threshold scan runs on one wave with DPP scans; the boundary
 //     refinement costs one workgroup barrier per 8-bit radix pass.
+#include <atomic>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -1288,6 +1290,42 @@ static int launch_select(const float* scores, int64_t ld, const int32_t* row_len
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   }
   return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
+}
+
+// Scratch for callers that cannot allocate (idx_select_translate_noalloc):
+// the long-row records live in this array, one copy per GPU, zero at load.
+// Every call leaves the first word of each 64 KiB block of the records it
+// used zero, as it does for a caller's workspace, which is all the next call
+// needs.  Host code never uses the array's name as an address: the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+static void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_addr[dev].store(p, std::memory_order_release);  // every thread finds the same address
+  }
+  return p;
+}
+
+int launch_select_translate_noalloc(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows,
+                                    int32_t max_len, int32_t k, const int32_t* req_row_ptr, int32_t num_req,
+                                    const int32_t* row_pos, int32_t c, const int32_t* page_table, int32_t pt_stride,
+                                    int32_t* sel, int32_t* sel_count, int32_t* out_slots, int32_t* out_pos,
+                                    int32_t* out_count, int32_t ld_out, hipStream_t stream) {
+  void* ws = nullptr;
+  if (topk_workspace_size(num_rows, max_len, k) > 0) {
+    ws = scratch_address();
+    if (ws == nullptr) return BS_ERR_LAUNCH;
+  }
+  const Translate tr{req_row_ptr, num_req, row_pos, c, page_table, pt_stride, out_slots, out_pos, out_count, ld_out};
+  return launch_select<true>(scores, ld, row_len, num_rows, max_len, k, sel, sel_count, ws, tr, stream);
 }
 
 int launch_topk(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows, int32_t max_len,

@@ -264,6 +264,34 @@ int idx_select_translate(const float* scores, int64_t ld_scores, const int32_t* 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * idx_select_translate_noalloc - idx_select_translate for callers that cannot
+ * allocate device memory: code under HIP graph capture that must not
+ * allocate, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, outputs, guarantees and errors as idx_select_translate,
+ * without the workspace: the long-row records (rows of >= 32,769 entries)
+ * live in a static device array of BS_NOALLOC_SCRATCH_BYTES per GPU, which
+ * the library holds until the process ends.  A call whose
+ * topk_workspace_bytes(num_rows, max_len, k) exceeds that size returns
+ * BS_ERR_WORKSPACE and launches nothing (128 KiB per row at
+ * max_len = 81,920, k = 2048: up to 64 such rows).  The call allocates and
+ * frees nothing; its first call on a device looks the array's address up
+ * (hipGetSymbolAddress) and keeps it.  The array is zero when the library is
+ * loaded, and every call leaves it as topk_select_rows leaves a workspace
+ * (the first word of every 64 KiB block zero), which is all the next call
+ * needs.  All calls on one GPU share its array: calls that overlap in
+ * time on one GPU (concurrent streams, threads) race and must not be made.
+ */
+#define BS_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int idx_select_translate_noalloc(const float* scores, int64_t ld_scores, const int32_t* row_len,
+                                 int32_t num_rows, int32_t max_len, int32_t k,
+                                 const int32_t* req_row_ptr, int32_t num_req, const int32_t* row_pos, int32_t c,
+                                 const int32_t* page_table, int32_t pt_stride,
+                                 int32_t* sel, int32_t* sel_count,
+                                 int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
+                                 void* stream);
+
+/*
  * idx_compress_store - compression of new raw index keys into the c = 4 key
  * cache the scorers read [QSA: the indexer's one shared key head; each 4 raw
  * index keys are averaged in FP32, normalised and rotated with the MRoPE

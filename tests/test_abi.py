@@ -223,3 +223,31 @@ def test_compress_validation():
         assert _compress(**{k: NULL}) == BS_ERR_NULL, k
     assert _compress(mpos=FAKE) == BS_ERR_NULL              # MRoPE positions need ring_pos
 
+
+def _noalloc(**kw):
+    a = dict(scores=FAKE, ld=81920, row_len=FAKE, num_rows=1, max_len=81920, k=2048, ptr=FAKE, num_req=1, pos=FAKE,
+             c=1, pt=FAKE, pt_stride=1280, sel=FAKE, cnt=FAKE, slots=FAKE, opos=NULL, ocnt=FAKE, ld_out=2048,
+             stream=NULL)
+    a.update(kw)
+    return bst.lib().idx_select_translate_noalloc(a["scores"], a["ld"], a["row_len"], a["num_rows"], a["max_len"],
+                                                  a["k"], a["ptr"], a["num_req"], a["pos"], a["c"], a["pt"],
+                                                  a["pt_stride"], a["sel"], a["cnt"], a["slots"], a["opos"],
+                                                  a["ocnt"], a["ld_out"], a["stream"])
+
+
+def test_noalloc_validation():
+    # host-side checks only: every case fails (or is a no-op) before anything is launched
+    assert _noalloc(num_rows=0) == BS_OK
+    assert _noalloc(k=0) == BS_ERR_ARG
+    assert _noalloc(c=2) == BS_ERR_ARG
+    assert _noalloc(ld_out=2047) == BS_ERR_ARG
+    assert _noalloc(ld=81919) == BS_ERR_ARG
+    assert _noalloc(num_req=0) == BS_ERR_ARG
+    for k in ("scores", "row_len", "sel", "cnt", "ptr", "pos", "pt", "slots", "ocnt"):
+        assert _noalloc(**{k: NULL}) == BS_ERR_NULL, k
+    # more long rows than the static scratch holds: rejected with the workspace status
+    per_row = bst.topk_workspace_bytes(1, 81920, 2048)
+    assert per_row > 0
+    too_many = bst.NOALLOC_SCRATCH_BYTES // per_row + 1
+    assert _noalloc(num_rows=too_many) == BS_ERR_WORKSPACE
+    assert "static scratch" in bst.status_string(BS_ERR_WORKSPACE)
