@@ -22,11 +22,14 @@ _lib = None
 
 
 def lib():
+    """The oracle library; ``ORACLE_LIB`` may name another build of the same
+    source (the sanitizer build in ``tests/test_oracle_sanitized.py``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB) or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC):
+        path = os.environ.get("ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and (not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
             _build.build()
-        L = C.CDLL(_build.LIB)
+        L = C.CDLL(path)
         P = C.c_void_p
         i32, i64 = C.c_int32, C.c_int64
         L.oracle_score.argtypes = [P, P, i64, P, i32, P, i32, P, i32, i32, P, i64, P]
