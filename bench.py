@@ -91,17 +91,22 @@ def cpu_baseline(inp, min_seconds: float):
     import oracle
     import synth
     topk_only = isinstance(inp, synth.ScoreRows)
+    select_only = isinstance(inp, synth.SelectBatch)
     reps, t0 = 0, time.perf_counter()
     while True:
         if topk_only:
             oracle.topk(inp.scores, inp.row_len, inp.k)
+        elif select_only:
+            sel, cnt = oracle.topk(inp.scores, inp.row_len, inp.inp.k)
+            oracle.expand_translate(inp.inp, sel, cnt)
         else:
             oracle.pipeline(inp)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or reps >= 5000:
             break
-    what = "top-k (full sort)" if topk_only else "score + top-k (full sort) + expand/translate"
+    what = ("top-k (full sort)" if topk_only else "top-k (full sort) + expand/translate" if select_only
+            else "score + top-k (full sort) + expand/translate")
     model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -273,6 +278,8 @@ def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
                              "algorithmic_bytes": alg, "avg_us": round(t_topk * 1e3, 2)}}
     if name == "qsa_indexshare_64req":
         return run_indexshare(name, inp, K, warmup, dev, stream)
+    if isinstance(inp, synth.SelectBatch):
+        return run_select_planned(name, inp, K, warmup, dev, stream)
     if isinstance(inp, synth.CompressInputs):
         return run_compress(name, inp, K, warmup, dev, stream)
     scorer = "prefill" if name == "qsa_prefill_8k" else "decode"
@@ -334,6 +341,65 @@ def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
         out["cold_note"] = ("median of 20 steps, each after writing a 512 MiB scratch buffer (flushes the 256 MB "
                             "Infinity Cache), outside the events")
     return out
+
+
+def run_select_planned(name, w, K, warmup, dev, stream):
+    """Selection + translation of a mixed batch on given FP32 rows, as the
+    layers of one step would run it: a step is two select+translate calls on
+    the same lengths (two layers).  Planned: topk_plan_rows once per step,
+    then two idx_select_translate_planned calls on its work list.  Unplanned
+    (reported beside it): two idx_select_translate calls, which size their
+    launch from max_len alone."""
+    import torch
+
+    import block_scoring_top_amd as bst
+    from synth.device import upload
+
+    inp = w.inp
+    d = upload(inp, dev)
+    R, L, k = w.num_rows, w.max_len, inp.k
+    s = torch.from_numpy(w.scores).to(dev)
+    rl = torch.from_numpy(w.row_len).to(dev)
+    sel = torch.empty((R, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty(R, dtype=torch.int32, device=dev)
+    slots = torch.empty((R, inp.ld_out), dtype=torch.int32, device=dev)
+    pos = torch.empty((R, inp.ld_out), dtype=torch.int32, device=dev)
+    oc = torch.empty(R, dtype=torch.int32, device=dev)
+    plan = bst.topk_plan(R, L, dev)
+    ws_p = bst.topk_planned_workspace(R, L, k, dev)
+    ws_u = bst.topk_workspace(R, L, k, dev)
+    mk_plan = bst.prepare_plan(rl, L, plan)
+    sel_p = bst.prepare_select_translate_planned(s, L, k, d.req_row_ptr, d.row_pos, inp.c, d.page_table, sel, cnt,
+                                                 slots, oc, plan, out_pos=pos, workspace=ws_p)
+    sel_u = bst.prepare_select_translate(s, rl, L, k, d.req_row_ptr, d.row_pos, inp.c, d.page_table, sel, cnt,
+                                         slots, oc, out_pos=pos, workspace=ws_u)
+    ms_p, kt_p = time_steps([mk_plan, sel_p, sel_p], K, warmup, stream, probe=1)
+    _, kt_plan = time_steps([mk_plan], max(K // 5, 2), 2, stream, probe=0)
+    ms_u, kt_u = time_steps([sel_u, sel_u], K, warmup, stream, probe=0)
+    torch.cuda.synchronize()
+    items = int(plan[0].item())
+    split = int(plan[1].item())
+    n_out = int(oc.sum().item())
+    t_sel = kt_p["burst_ms"]
+    # one launch: every row read once up to its length, the selection, the
+    # slots and positions written
+    alg = int(w.row_len.astype("int64").sum()) * 4 + R * k * 4 + n_out * 8 + R * 8
+    ach = alg / (t_sel * 1e-3) / 1e9
+    log(f"{name}: planned {ms_p * 1e3:.1f} us/step (plan {kt_plan['burst_ms'] * 1e3:.1f} us, select "
+        f"{t_sel * 1e3:.1f} us x 2; {items} items, split from {split}); unplanned {ms_u * 1e3:.1f} us/step "
+        f"(select {kt_u['burst_ms'] * 1e3:.1f} us x 2)")
+    return {"_inp": w, "rows_per_s": round(2 * R / (ms_p * 1e-3), 1), "ms_per_step": round(ms_p, 5),
+            "unplanned_ms_per_step": round(ms_u, 5),
+            "config": {"workload": name, "rows": R, "long_rows": int((w.row_len >= 32769).sum()),
+                       "max_len": L, "k": k, "c": inp.c, "page_tokens": 64, "plan_items": items,
+                       "split_from": split,
+                       "steps": "plan once, then select+translate twice (two layers on the same lengths); "
+                                "rows/s counts both calls' rows"},
+            "kernels_us": {"plan": round(kt_plan["burst_ms"] * 1e3, 2), "select_planned": round(t_sel * 1e3, 2),
+                           "select_unplanned": round(kt_u["burst_ms"] * 1e3, 2)},
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "topk_planned_kernel", "algorithmic_bytes": alg, "avg_us": round(t_sel * 1e3, 2)}}
 
 
 def run_indexshare(name, inp, K, warmup, dev, stream):

@@ -9,8 +9,10 @@ module raises on first use.
 
 Steps (same names as the C ABI):
   idx_score_decode / idx_score_prefill  ->  topk_select_rows  ->  idx_expand_translate
-  (idx_select_translate: the last two in one kernel; idx_expand_translate_shared:
-  the expansion of a selection reused across speculative draft steps)
+  (idx_select_translate: the last two in one kernel; topk_plan_rows +
+  idx_select_translate_planned: the same over a work list built once per step
+  from the row lengths; idx_expand_translate_shared: the expansion of a
+  selection reused across speculative draft steps)
 """
 from __future__ import annotations
 
@@ -65,6 +67,15 @@ def lib():
         L.idx_select_translate_noalloc.argtypes = [P, i64, P, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P, P,
                                                    i32, P]
         L.idx_select_translate_noalloc.restype = C.c_int
+        L.topk_plan_bytes.argtypes = [i32, i32]
+        L.topk_plan_bytes.restype = C.c_size_t
+        L.topk_planned_workspace_bytes.argtypes = [i32, i32, i32]
+        L.topk_planned_workspace_bytes.restype = C.c_size_t
+        L.topk_plan_rows.argtypes = [P, i32, i32, P, C.c_size_t, P]
+        L.topk_plan_rows.restype = C.c_int
+        L.idx_select_translate_planned.argtypes = [P, i64, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P, P,
+                                                   i32, P, C.c_size_t, P, C.c_size_t, P]
+        L.idx_select_translate_planned.restype = C.c_int
         L.idx_compress_store.argtypes = [P, i32, P, P, P, i32, i32, i32, i32, i32, i32, C.c_double, P, P, P, i32,
                                          P, i64, P]
         L.idx_compress_store.restype = C.c_int
@@ -241,7 +252,7 @@ def _select_translate_args(scores, row_len, max_len, k, req_row_ptr, row_pos, c,
     R = int(scores.shape[0])
     if sel.dim() != 2 or sel.shape[0] != R or sel.shape[1] != k:
         raise ValueError("sel must be [num_rows, k]")
-    if sel_count.numel() != R or row_len.numel() != R or row_pos.numel() != R:
+    if sel_count.numel() != R or row_pos.numel() != R or (row_len is not None and row_len.numel() != R):
         raise ValueError("row_len, row_pos and sel_count must hold num_rows entries")
     if out_slots.dim() != 2 or out_slots.shape[0] != R:
         raise ValueError("out_slots must be [num_rows, ld_out]")
@@ -273,6 +284,57 @@ def idx_select_translate_noalloc(scores, row_len, max_len, k, req_row_ptr, row_p
     args = _select_translate_args(scores, row_len, max_len, k, req_row_ptr, row_pos, c, page_table, sel,
                                   sel_count, out_slots, out_count, out_pos, None)[:-2]
     _check(lib().idx_select_translate_noalloc(*args, _stream(stream, scores.device)), "idx_select_translate_noalloc")
+
+
+def topk_plan_bytes(num_rows: int, max_len: int) -> int:
+    return int(lib().topk_plan_bytes(int(num_rows), int(max_len)))
+
+
+def topk_planned_workspace_bytes(num_rows: int, max_len: int, k: int) -> int:
+    return int(lib().topk_planned_workspace_bytes(int(num_rows), int(max_len), int(k)))
+
+
+def topk_plan(num_rows: int, max_len: int, device) -> torch.Tensor:
+    """Storage for a plan (int32, uninitialised: ``topk_plan_rows`` fills it)."""
+    n = topk_plan_bytes(num_rows, max_len)
+    return torch.empty(max(1, (n + 3) // 4), dtype=torch.int32, device=device)
+
+
+def topk_planned_workspace(num_rows: int, max_len: int, k: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace for ``idx_select_translate_planned`` (None if none)."""
+    n = topk_planned_workspace_bytes(num_rows, max_len, k)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _plan_args(row_len, max_len, plan):
+    dev = row_len.device
+    return (_ptr(row_len, _I32, "row_len", dev), int(row_len.numel()), int(max_len), _ptr(plan, _I32, "plan", dev),
+            plan.numel() * plan.element_size())
+
+
+def topk_plan_rows(row_len, max_len, plan, stream=None):
+    """Build the selection's work list from the row lengths.  See
+    ``topk_plan_rows`` in blockscore.h."""
+    _check(lib().topk_plan_rows(*_plan_args(row_len, max_len, plan), _stream(stream, row_len.device)),
+           "topk_plan_rows")
+
+
+def _select_translate_planned_args(scores, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                                   out_slots, out_count, plan, out_pos=None, workspace=None):
+    # The argument tuple of idx_select_translate with row_len taken out and the
+    # plan put before the workspace.
+    a = _select_translate_args(scores, None, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                               out_slots, out_count, out_pos, workspace)
+    return (*a[:2], *a[3:18], _ptr(plan, _I32, "plan", scores.device), plan.numel() * plan.element_size(), *a[18:])
+
+
+def idx_select_translate_planned(scores, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                                 out_slots, out_count, plan, out_pos=None, workspace=None, stream=None):
+    """``idx_select_translate`` over the work list of a plan (the plan's row
+    lengths).  See ``idx_select_translate_planned`` in blockscore.h."""
+    args = _select_translate_planned_args(scores, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                                          out_slots, out_count, plan, out_pos, workspace)
+    _check(lib().idx_select_translate_planned(*args, _stream(stream, scores.device)), "idx_select_translate_planned")
 
 
 def _compress_args(k_raw, req_tok_ptr, tok_start, mrope_pos, max_tok, rotary_dim, sections, theta, ring,
@@ -359,12 +421,28 @@ def prepare_select_translate(scores, row_len, max_len, k, req_row_ptr, row_pos, 
                         scores.device)
 
 
+def prepare_plan(row_len, max_len, plan) -> PreparedCall:
+    """``topk_plan_rows`` with fixed arguments."""
+    return PreparedCall("topk_plan_rows", _plan_args(row_len, max_len, plan), row_len.device)
+
+
+def prepare_select_translate_planned(scores, max_len, k, req_row_ptr, row_pos, c, page_table, sel, sel_count,
+                                     out_slots, out_count, plan, out_pos=None, workspace=None) -> PreparedCall:
+    """``idx_select_translate_planned`` with fixed arguments."""
+    return PreparedCall("idx_select_translate_planned",
+                        _select_translate_planned_args(scores, max_len, k, req_row_ptr, row_pos, c, page_table, sel,
+                                                       sel_count, out_slots, out_count, plan, out_pos, workspace),
+                        scores.device)
+
+
 __all__ = [
     "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
     "topk_select_rows", "idx_expand_translate", "idx_expand_translate_shared", "idx_select_translate",
     "idx_select_translate_noalloc", "NOALLOC_SCRATCH_BYTES", "idx_compress_store", "status_string", "BlockScoreError",
     "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate", "prepare_expand_shared",
-    "prepare_compress_store",
+    "prepare_compress_store", "topk_plan_bytes", "topk_planned_workspace_bytes", "topk_plan",
+    "topk_planned_workspace", "topk_plan_rows", "idx_select_translate_planned", "prepare_plan",
+    "prepare_select_translate_planned",
 ]
 
 

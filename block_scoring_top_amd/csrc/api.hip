@@ -80,6 +80,58 @@ BS_EXPORT int topk_select_rows(const float* scores, int64_t ld_scores, const int
                          static_cast<hipStream_t>(stream));
 }
 
+BS_EXPORT size_t topk_plan_bytes(int32_t num_rows, int32_t max_len) {
+  if (num_rows <= 0 || max_len < 0) return 0;
+  return bs::topk_plan_bytes(num_rows, max_len);
+}
+
+BS_EXPORT size_t topk_planned_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k) {
+  if (num_rows <= 0 || max_len <= 0) return 0;
+  return bs::topk_planned_workspace_size(num_rows, max_len, k);
+}
+
+namespace {
+// The planned selection launches one 512-lane workgroup per plan slot (at
+// most 2^22 slots keeps the grid under 2^31 lanes) and addresses a row with a
+// buffer of 32-bit byte range.
+inline bool plan_shape_ok(int32_t num_rows, int32_t max_len) {
+  return (int64_t)max_len <= (int64_t)65535 * 4096 && bs::topk_plan_items(num_rows, max_len) <= ((size_t)1 << 22);
+}
+}  // namespace
+
+BS_EXPORT int topk_plan_rows(const int32_t* row_len, int32_t num_rows, int32_t max_len, int32_t* plan,
+                             size_t plan_bytes, void* stream) {
+  if (num_rows < 0 || max_len < 0) return BS_ERR_ARG;
+  if (num_rows == 0) return BS_OK;
+  if (!row_len || !plan) return BS_ERR_NULL;
+  if (!plan_shape_ok(num_rows, max_len)) return BS_ERR_ARG;
+  if (plan_bytes < bs::topk_plan_bytes(num_rows, max_len)) return BS_ERR_WORKSPACE;
+  return bs::launch_topk_plan(row_len, num_rows, max_len, plan, static_cast<hipStream_t>(stream));
+}
+
+BS_EXPORT int idx_select_translate_planned(const float* scores, int64_t ld_scores, int32_t num_rows, int32_t max_len,
+                                           int32_t k, const int32_t* req_row_ptr, int32_t num_req,
+                                           const int32_t* row_pos, int32_t c, const int32_t* page_table,
+                                           int32_t pt_stride, int32_t* sel, int32_t* sel_count, int32_t* out_slots,
+                                           int32_t* out_pos, int32_t* out_count, int32_t ld_out, const int32_t* plan,
+                                           size_t plan_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_rows < 0 || num_req < 0 || max_len < 0 || k < 1 || k > BS_KMAX) return BS_ERR_ARG;
+  if (c != 1 && c != 4) return BS_ERR_ARG;
+  if ((int64_t)ld_out < (int64_t)k * c + c - 1) return BS_ERR_ARG;
+  if (num_rows == 0) return BS_OK;
+  if (num_req == 0) return BS_ERR_ARG;
+  if (!scores || !plan || !sel || !sel_count || !req_row_ptr || !row_pos || !page_table || !out_slots || !out_count)
+    return BS_ERR_NULL;
+  if (ld_scores < (int64_t)max_len || pt_stride < 1) return BS_ERR_ARG;
+  if (!plan_shape_ok(num_rows, max_len)) return BS_ERR_ARG;
+  if (plan_bytes < bs::topk_plan_bytes(num_rows, max_len)) return BS_ERR_WORKSPACE;
+  const size_t need = bs::topk_planned_workspace_size(num_rows, max_len, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return BS_ERR_WORKSPACE;
+  return bs::launch_select_translate_planned(scores, ld_scores, num_rows, max_len, k, req_row_ptr, num_req, row_pos, c,
+                                             page_table, pt_stride, sel, sel_count, out_slots, out_pos, out_count,
+                                             ld_out, plan, workspace, static_cast<hipStream_t>(stream));
+}
+
 BS_EXPORT int idx_expand_translate(const int32_t* sel, const int32_t* sel_count, int32_t k,
                                    const int32_t* req_row_ptr, int32_t num_req,
                                    const int32_t* row_pos, int32_t num_rows, int32_t c,

@@ -42,6 +42,18 @@ int launch_select_translate_noalloc(const float* scores, int64_t ld, const int32
                                     int32_t* sel, int32_t* sel_count, int32_t* out_slots, int32_t* out_pos,
                                     int32_t* out_count, int32_t ld_out, hipStream_t stream);
 
+// Planned selection: the plan's size and the workspace the planned launch
+// needs, the planning launch, and the selection driven by a plan.
+size_t topk_plan_items(int32_t num_rows, int32_t max_len);
+size_t topk_plan_bytes(int32_t num_rows, int32_t max_len);
+size_t topk_planned_workspace_size(int32_t num_rows, int32_t max_len, int32_t k);
+int launch_topk_plan(const int32_t* row_len, int32_t num_rows, int32_t max_len, int32_t* plan, hipStream_t stream);
+int launch_select_translate_planned(const float* scores, int64_t ld, int32_t num_rows, int32_t max_len, int32_t k,
+                                    const int32_t* req_row_ptr, int32_t num_req, const int32_t* row_pos, int32_t c,
+                                    const int32_t* page_table, int32_t pt_stride, int32_t* sel, int32_t* sel_count,
+                                    int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
+                                    const int32_t* plan, void* workspace, hipStream_t stream);
+
 // row_pos_now == nullptr: the plain expansion; otherwise the IndexShare one
 // (tail through row_pos_now[r], at most max_advance past row_pos[r]).
 int launch_expand(const int32_t* sel, const int32_t* sel_count, int32_t k,

@@ -25,24 +25,32 @@
 //     bin, not its value, and marks the entries above and in the boundary bin
 //     with two bit masks;
 //   * long rows (>= 32,769 entries, any number of rows): one launch, one
-//     1,024-lane workgroup per 16,384-entry chunk, the chunk in registers.
-//     In place of the cluster's merged histogram, each chunk builds its own
-//     histogram and keeps as candidates every entry at or above the bin of
-//     its local q-th largest, q a little above the chunk's expected share of
-//     the row's top k; it publishes them with their bin floor and arrives on
-//     the row's counter.  The last chunk to arrive merges the candidates'
-//     histogram in LDS, finds the threshold bin, emits the entries above it
-//     and refines the boundary bin exactly.  The candidates are the whole row
-//     at and above the threshold bin whenever that bin is not below any
-//     chunk's floor (checked; otherwise the same workgroup selects the whole
-//     row by streaming it), so the result is exact in every case.  No
-//     workgroup waits on another (no co-residency assumption) and no
-//     device-scope fence is issued: on gfx950 such a fence writes back and
-//     invalidates the per-XCD L2, which measured far costlier than the whole
-//     kernel;
+//     512-lane workgroup per 8,192-entry chunk, the chunk in registers (the
+//     launch's rows shorter than that are each selected whole by their first
+//     workgroup).  In place of the cluster's merged histogram, each chunk
+//     builds its own histogram and keeps as candidates every entry at or
+//     above the bin of its local q-th largest, q a little above the chunk's
+//     expected share of the row's top k; it publishes them with its
+//     histogram and bin floor and arrives on the row's counter.  The last
+//     chunk to arrive sums the published histograms, finds the threshold
+//     bin, emits the candidates above it and refines the boundary bin
+//     exactly.  The candidates are the whole row at and above the threshold
+//     bin whenever that bin is not below any chunk's floor (checked;
+//     otherwise the same workgroup selects the whole row by streaming it), so
+//     the result is exact in every case.  No workgroup waits on another (no
+//     co-residency assumption) and no device-scope fence is issued: on
+//     gfx950 such a fence writes back and invalidates the per-XCD L2, which
+//     measured far costlier than the whole kernel;
+//   * planned (the blog's planning kernel): one small kernel turns the row
+//     lengths into a work list of whole-row and chunk items and picks the
+//     length from which rows are split; the selection then runs one
+//     workgroup per item, reading each row only up to its length, and every
+//     call on the same lengths reuses the list;
 //   * emission is count, block scan, write (no per-entry atomics); the
-//     threshold scan runs on one wave with DPP scans; the boundary
-//     refinement costs one workgroup barrier per 8-bit radix pass.
+//     threshold scan runs on one wave with DPP scans (block-wide on long
+//     rows); the boundary refinement costs one workgroup barrier per 8-bit
+//     radix pass.
+#include <algorithm>
 #include <atomic>
 
 #include "device.h"
@@ -113,9 +121,11 @@ __host__ __device__ constexpr size_t ck_cand_offset(int wmax) {
 // layout sits on the first word of such a block: a call that leaves those
 // words zero leaves the workspace ready for any later shape.
 constexpr size_t kWsBlock = (size_t)64 << 10;
-static size_t ck_record_bytes(int32_t max_len, int32_t k) {
+// min_cut: the shortest row the launch may split (the per-chunk slots only
+// shrink as rows grow).
+static size_t ck_record_bytes(int32_t max_len, int32_t k, int32_t min_cut = kLongMin) {
   const int wmax = (max_len + kCkChunk - 1) / kCkChunk;
-  const size_t b = ck_cand_offset(wmax) + (size_t)wmax * ck_slots<kCkChunk>(kLongMin, k) * 8;
+  const size_t b = ck_cand_offset(wmax) + (size_t)wmax * ck_slots<kCkChunk>(min_cut, k) * 8;
   return (b + kWsBlock - 1) / kWsBlock * kWsBlock;
 }
 
@@ -1033,32 +1043,39 @@ __device__ __forceinline__ uint64_t ws_load64(const uint64_t* p) {
 // scan, LDS) and refined in bin T on the composite (FP32 key, inverted
 // index); then the selection is written out and translated, and the row's
 // arrival counter is reset for the next call.
-template <bool TRANSLATE, int NT>
-__global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
-    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
-    int64_t rec_bytes, int32_t wmax, Translate tr) {
+// One work item of the long-row selection: chunk w of row r, for a row of at
+// least `cut` entries.  Without KNOWN_N the length is read from row_len while
+// the chunk's score loads are in flight, and a shorter row is selected whole
+// by its w == 0 item (its other items do nothing); with KNOWN_N the caller
+// gives the length and passes only chunks of rows split at `cut`.  All lanes
+// call; every return is uniform.
+template <bool TRANSLATE, int NT, bool KNOWN_N>
+__device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_given, int cut,
+                                           const float* __restrict__ scores, int64_t ld,
+                                           const int32_t* __restrict__ row_len, int32_t max_len, int32_t k,
+                                           int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+                                           uint8_t* __restrict__ ws, int64_t rec_bytes, int32_t wmax,
+                                           const Translate& tr) {
   constexpr int VPT = kCkVpt, CH = NT * VPT, B = kBins / NT, P = VPT / 2, PA = kCkAll / NT;
   static_assert(B == 2, "the published histogram packs each lane's two bins into one 32-bit store");
   static_assert(CH <= 65535, "a chunk's per-bin counts fit 16 bits");
-  __shared__ ChunkShared cs;
   TopkShared<kCkCand, kCkPages>& s = cs.t;
-  const int r = blockIdx.x, w = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int lo = w * CH;
   const float* row = scores + (int64_t)r * ld;
   // The chunk's loads go out with the row-length read (the row holds
   // max_len readable entries); entries at or past the length are masked.
-  const RowReader rdx(row, max_len);
+  const RowReader rdx(row, KNOWN_N ? n_given : max_len);
   float x[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) x[i] = rdx.at(tid, lo + i * NT);
-  const int n = max(0, min(row_len[r], max_len));
+  const int n = KNOWN_N ? n_given : max(0, min(row_len[r], max_len));
   int32_t* out = sel + (int64_t)r * k;
   // The branches on the row length come after the binning below, which
   // consumes the loads above: left before it, they let the compiler sink
   // the loads into the branch, after the length's round trip.
   const int nchunk = (n + CH - 1) / CH;
-  const int qn = ck_quota<CH>(max(n, kLongMin), k);  // used only when n >= kLongMin
+  const int qn = ck_quota<CH>(max(n, cut), k);  // used only when n >= cut
   const int Q = ck_slots_for(qn);
   const int nck = min(CH, n - lo);
   const uint32_t q = (uint32_t)min(qn, nck);
@@ -1096,7 +1113,7 @@ __global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
     pb[p] = code;
   }
   __syncthreads();
-  if (n < kLongMin) {
+  if (!KNOWN_N && n < cut) {
     if (w == 0) select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, min(k, n), k, out, sel_count, r, tr);
     return;
   }
@@ -1264,7 +1281,236 @@ __global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
     ws_store32(reinterpret_cast<uint32_t*>(rec + (size_t)i * kWsBlock), 0u);
 }
 
+// One workgroup per (row, chunk) of the grid; rows shorter than kLongMin are
+// selected whole by their first workgroup.
+template <bool TRANSLATE, int NT>
+__global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
+    int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
+    int64_t rec_bytes, int32_t wmax, Translate tr) {
+  __shared__ ChunkShared cs;
+  chunk_item<TRANSLATE, NT, false>(cs, blockIdx.x, blockIdx.y, 0, kLongMin, scores, ld, row_len, max_len, k, sel,
+                                   sel_count, ws, rec_bytes, wmax, tr);
+}
+
+// Planning (TopK-V2: a planning kernel reads the batch's row lengths once,
+// picks the length from which rows are split over several workgroups, and
+// lays out the work list the selection's workgroups take their items from;
+// the list serves every call on the same lengths, e.g. all layers of one
+// step).
+//
+// The plan: a header of kPlanHeader int32 (item count, the split length,
+// num_rows, max_len, chunk item count), then the items, one int4 {row,
+// chunk, length, 0} each: first one item per kCkChunk-entry chunk of every
+// row at least the split length long (in row order), then one item per
+// shorter row, chunk kPlanWhole (selected whole: in registers up to
+// kCkChunk entries, streamed past that).  Split rows come first so that
+// their chains (chunks, then the resolution) start before the short rows.
+//
+// The split length: kPlanMinCut (rows of three or more chunks are split) when
+// the resulting items all fit on the device at once (`pool` workgroups: the
+// compute units times the selection's workgroups per unit), which shortens
+// the longest item while units would otherwise idle; kLongMin (five or more
+// chunks) otherwise, where the rows alone keep every unit busy and a split
+// only adds the resolution's extra round trips.
+constexpr int kPlanNT = 1024;
+constexpr int kPlanRegs = 4;  // rows per lane kept in registers between the passes
+constexpr int kPlanWhole = -1;
+constexpr int kPlanMinCut = 2 * kCkChunk + 1;
+constexpr int kPlanHeader = 8;  // int32 words before the items (16-byte aligned)
+static_assert(kPlanMinCut <= kLongMin, "the split lengths the planner picks between");
+
+__device__ __forceinline__ uint32_t plan_chunks_of(int n) { return (uint32_t)((n + kCkChunk - 1) / kCkChunk); }
+
+// Block-wide exclusive scan of one value per lane (kPlanNT lanes); `tot`
+// receives the block's total.  Two barriers; `sh` holds kPlanNT / 64 words.
+__device__ __forceinline__ uint32_t plan_block_scan(uint32_t x, uint32_t* sh, uint32_t& tot) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(x);
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  uint32_t off = 0;
+  tot = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanNT / 64; ++w) {
+    off += w < wave ? sh[w] : 0u;
+    tot += sh[w];
+  }
+  __syncthreads();
+  return off + incl - x;
+}
+
+__global__ __launch_bounds__(kPlanNT) void topk_plan_kernel(const int32_t* __restrict__ row_len, int32_t num_rows,
+                                                            int32_t max_len, int32_t pool,
+                                                            int32_t* __restrict__ plan) {
+  __shared__ uint32_t red[3][kPlanNT / 64];
+  __shared__ uint32_t scan_c[kPlanNT / 64], scan_w[kPlanNT / 64];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  // Pass 1: per lane, the rows tid, tid + kPlanNT, ... (the first kPlanRegs
+  // kept): items at the low split length, and chunk items at either length.
+  int nreg[kPlanRegs];
+  uint32_t items_lo = 0, chunks_lo = 0, chunks_hi = 0;
+  auto count = [&](int n) {
+    const uint32_t ch = plan_chunks_of(n);
+    items_lo += n >= kPlanMinCut ? ch : 1u;
+    chunks_lo += n >= kPlanMinCut ? ch : 0u;
+    chunks_hi += n >= kLongMin ? ch : 0u;
+  };
+#pragma unroll
+  for (int i = 0; i < kPlanRegs; ++i) {
+    const int r = i * kPlanNT + tid;
+    nreg[i] = r < num_rows ? max(0, min(row_len[r], max_len)) : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kPlanRegs; ++i)
+    if (nreg[i] >= 0) count(nreg[i]);
+  for (int r = kPlanRegs * kPlanNT + tid; r < num_rows; r += kPlanNT) count(max(0, min(row_len[r], max_len)));
+  // The three totals: wave sums, then one barrier.
+  items_lo = wave_incl_scan(items_lo);
+  chunks_lo = wave_incl_scan(chunks_lo);
+  chunks_hi = wave_incl_scan(chunks_hi);
+  if (lane == 63) {
+    red[0][wave] = items_lo;
+    red[1][wave] = chunks_lo;
+    red[2][wave] = chunks_hi;
+  }
+  __syncthreads();
+  uint32_t t_items = 0, t_lo = 0, t_hi = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanNT / 64; ++w) {
+    t_items += red[0][w];
+    t_lo += red[1][w];
+    t_hi += red[2][w];
+  }
+  const bool low = t_items <= (uint32_t)pool;
+  const int cut = low ? kPlanMinCut : kLongMin;
+  const uint32_t total_chunks = low ? t_lo : t_hi;
+  // Pass 2: chunk items at base_c + their rank, whole-row items after every
+  // chunk item.
+  int4* items = reinterpret_cast<int4*>(plan + kPlanHeader);
+  uint32_t base_c = 0, base_w = total_chunks;
+  // One block of kPlanNT rows (r0 uniform; n < 0 past the last row).
+  auto place = [&](int r0, int n) {
+    const int r = r0 + tid;
+    const bool split = n >= cut, whole = n >= 0 && !split;
+    const uint32_t cc = split ? plan_chunks_of(n) : 0u;
+    uint32_t tc, tw;
+    const uint32_t oc = base_c + plan_block_scan(cc, scan_c, tc);
+    const uint32_t ow = base_w + plan_block_scan(whole ? 1u : 0u, scan_w, tw);
+    for (uint32_t c = 0; c < cc; ++c) items[oc + c] = int4{r, (int)c, n, 0};
+    if (whole) items[ow] = int4{r, kPlanWhole, n, 0};
+    base_c += tc;
+    base_w += tw;
+  };
+#pragma unroll
+  for (int i = 0; i < kPlanRegs; ++i)
+    if (i * kPlanNT < num_rows) place(i * kPlanNT, nreg[i]);
+  for (int r0 = kPlanRegs * kPlanNT; r0 < num_rows; r0 += kPlanNT) {
+    const int r = r0 + tid;
+    place(r0, r < num_rows ? max(0, min(row_len[r], max_len)) : -1);
+  }
+  if (tid == 0) {
+    plan[0] = (int32_t)base_w;
+    plan[1] = cut;
+    plan[2] = num_rows;
+    plan[3] = max_len;
+    plan[4] = (int32_t)total_chunks;
+  }
+}
+
+// The planned selection: one workgroup per slot of the work list, the slots
+// past the plan's item count exiting at once.  The hardware dispatcher acts
+// as the persistent pool: it starts a workgroup on a compute unit as soon as
+// one retires there, and items never wait on each other (a split row is
+// resolved by whichever of its chunks arrives last).  A software loop over
+// items in each workgroup was measured against it at compile time: the loop
+// keeps its per-lane invariants live across iterations and needs 195 VGPRs
+// (one workgroup per compute unit) where one item per workgroup needs 111
+// (two).
+template <bool TRANSLATE, int NT>
+__global__ __launch_bounds__(NT, 1) void topk_planned_kernel(
+    const float* __restrict__ scores, int64_t ld, int32_t num_rows, int32_t max_len, int32_t k,
+    int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws, int64_t rec_bytes,
+    int32_t wmax, const int32_t* __restrict__ plan, Translate tr) {
+  __shared__ ChunkShared cs;
+  // The item count, the split length and this slot's item in one round trip
+  // (the grid has one workgroup per slot of the plan, so the read is in
+  // bounds).
+  const int total = plan[0];
+  const int cut = max(plan[1], kPlanMinCut);
+  const int4 cur = reinterpret_cast<const int4*>(plan + kPlanHeader)[blockIdx.x];
+  if ((int)blockIdx.x >= total) return;
+  const int r = cur.x, n = max(0, min(cur.z, max_len));
+  if ((unsigned)r >= (unsigned)num_rows) return;  // never, for a plan made for this batch
+  if (cur.y == kPlanWhole) {
+    select_whole_row<NT, kCkVpt, kCkCand, TRANSLATE>(cs.t, scores + (int64_t)r * ld, n, min(k, n), k,
+                                                     sel + (int64_t)r * k, sel_count, r, tr);
+  } else if (n >= cut && (unsigned)cur.y < (unsigned)min(wmax, (n + kCkChunk - 1) / kCkChunk)) {
+    chunk_item<TRANSLATE, NT, true>(cs, r, cur.y, n, cut, scores, ld, nullptr, max_len, k, sel, sel_count, ws,
+                                    rec_bytes, wmax, tr);
+  }
+}
+
 static bool use_long_path(int32_t max_len) { return max_len >= kLongMin; }
+
+constexpr int kMaxDevices = 64;
+
+size_t topk_plan_items(int32_t num_rows, int32_t max_len) {
+  const int64_t per_row = max_len >= kPlanMinCut ? (max_len + kCkChunk - 1) / kCkChunk : 1;
+  return (size_t)num_rows * (size_t)per_row;
+}
+
+size_t topk_plan_bytes(int32_t num_rows, int32_t max_len) {
+  return (size_t)kPlanHeader * 4 + topk_plan_items(num_rows, max_len) * sizeof(int4);
+}
+static_assert(kPlanHeader * 4 % sizeof(int4) == 0, "items stay 16-byte aligned");
+
+size_t topk_planned_workspace_size(int32_t num_rows, int32_t max_len, int32_t k) {
+  return max_len >= kPlanMinCut ? (size_t)num_rows * ck_record_bytes(max_len, k, kPlanMinCut) : 0;
+}
+
+// Workgroups of the planned selection the current device holds at once
+// (compute units times resident workgroups per unit), found once per device;
+// the planner splits more rows while the items fit in it.
+static std::atomic<int> g_pool[kMaxDevices];
+
+static int planned_pool() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int pool = g_pool[dev].load(std::memory_order_relaxed);
+  if (pool == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(
+                                                               &topk_planned_kernel<true, kCkNT>),
+                                                     kCkNT, 0) != hipSuccess)
+      return 0;
+    pool = std::max(1, cus) * std::max(1, occ);
+    g_pool[dev].store(pool, std::memory_order_relaxed);
+  }
+  return pool;
+}
+
+int launch_topk_plan(const int32_t* row_len, int32_t num_rows, int32_t max_len, int32_t* plan, hipStream_t stream) {
+  const int pool = planned_pool();
+  if (pool <= 0) return BS_ERR_LAUNCH;
+  hipLaunchKernelGGL(topk_plan_kernel, dim3(1), dim3(kPlanNT), 0, stream, row_len, num_rows, max_len, pool, plan);
+  return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
+}
+
+int launch_select_translate_planned(const float* scores, int64_t ld, int32_t num_rows, int32_t max_len, int32_t k,
+                                    const int32_t* req_row_ptr, int32_t num_req, const int32_t* row_pos, int32_t c,
+                                    const int32_t* page_table, int32_t pt_stride, int32_t* sel, int32_t* sel_count,
+                                    int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
+                                    const int32_t* plan, void* workspace, hipStream_t stream) {
+  const Translate tr{req_row_ptr, num_req, row_pos, c, page_table, pt_stride, out_slots, out_pos, out_count, ld_out};
+  const int grid = (int)topk_plan_items(num_rows, max_len);
+  const int wmax = std::max(1, (max_len + kCkChunk - 1) / kCkChunk);
+  const int64_t rec = max_len >= kPlanMinCut ? (int64_t)ck_record_bytes(max_len, k, kPlanMinCut) : 0;
+  hipLaunchKernelGGL((topk_planned_kernel<true, kCkNT>), dim3(grid), dim3(kCkNT), 0, stream, scores, ld, num_rows,
+                     max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace), rec, wmax, plan, tr);
+  return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
+}
 
 size_t topk_workspace_size(int32_t num_rows, int32_t max_len, int32_t k) {
   return use_long_path(max_len) ? (size_t)num_rows * ck_record_bytes(max_len, k) : 0;
@@ -1300,7 +1546,6 @@ static int launch_select(const float* scores, int64_t ld, const int32_t* row_len
 // address comes from hipGetSymbolAddress, once per device.
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
-constexpr int kMaxDevices = 64;
 static std::atomic<void*> g_scratch_addr[kMaxDevices];
 
 static void* scratch_address() {

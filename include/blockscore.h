@@ -6,6 +6,8 @@
  *   2. select  - topk_select_rows
  *   3. expand  - idx_expand_translate
  * plus idx_select_translate (steps 2 and 3 in one kernel),
+ * topk_plan_rows + idx_select_translate_planned (the same over a work list
+ * built once per step from the row lengths),
  * idx_expand_translate_shared (step 3 for a selection reused across
  * speculative draft steps) and idx_compress_store (the step before 1: raw
  * index keys compressed into the c = 4 key cache).
@@ -171,9 +173,11 @@ size_t topk_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k);
  * to an order-preserving 16-bit key whose upper 10 bits index a 1,024-bin
  * histogram; the bin holding the m-th largest is located, entries in higher
  * bins are emitted directly, and the boundary bin is resolved exactly on the
- * (FP32 key, index) pair by radix selection.  A row of up to 32,768
- * entries is done by one workgroup, in registers.  A longer row is split over
- * one workgroup per 16,384 entries: each keeps the entries at or above the
+ * (FP32 key, index) pair by radix selection.  With max_len <= 32,768 every
+ * row is done by one workgroup, in registers.  Otherwise a row shorter than
+ * 32,769 entries is still done by one workgroup (streamed past 8,192
+ * entries), and a longer row is split over one workgroup per 8,192 entries:
+ * each keeps the entries at or above the
  * histogram bin of its local q-th largest (q a little above its share of the
  * row's top k) as candidates and publishes them; the last to arrive builds
  * the candidates' histogram, selects the threshold bin and resolves it, after
@@ -290,6 +294,61 @@ int idx_select_translate_noalloc(const float* scores, int64_t ld_scores, const i
                                  int32_t* sel, int32_t* sel_count,
                                  int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
                                  void* stream);
+
+/*
+ * Planned selection [TOPK: a planning kernel reads the batch's length
+ * distribution, picks the length from which rows are split over several
+ * workgroups, and builds a work list that serves every DSA layer of the
+ * forward pass].
+ *
+ * topk_plan_bytes - bytes of a plan for (num_rows, max_len): 32 + 16 per
+ * work-list slot, one slot per row, or ceil(max_len / 8,192) per row when
+ * max_len >= 16,385.  0 for num_rows <= 0.
+ *
+ * topk_planned_workspace_bytes - the workspace idx_select_translate_planned
+ * needs: records as described at topk_workspace_bytes, sized for rows split
+ * from 16,385 entries on, when max_len >= 16,385; else 0 (none needed).  The
+ * same zero-fill-once contract: every call leaves the first 4 bytes of every
+ * 64 KiB block zero.
+ *
+ * topk_plan_rows - one single-workgroup kernel that reads row_len[0 ..
+ * num_rows-1] (clamped to 0 .. max_len) and writes the plan into `plan`
+ * (device memory of at least topk_plan_bytes, owned by the caller; its
+ * contents are internal).  The split length is 16,385 when the items that it
+ * gives fit on the device at once (compute units times the selection's
+ * resident workgroups per unit), else 32,769.  Every row shorter than the
+ * split length is one item selected whole by one workgroup; a longer one is
+ * one item per 8,192-entry chunk, resolved as in topk_select_rows.  The
+ * chunk items come first in the list, so split rows start first.  The plan
+ * depends on the lengths and max_len only (not on k, the scores or the
+ * translation), so it is built once per step and passed to every
+ * selection of that step.  Returns BS_OK, BS_ERR_NULL, BS_ERR_ARG (negative
+ * counts, max_len > 65535*4096, more than 2^22 slots), BS_ERR_WORKSPACE
+ * (plan_bytes too small) or BS_ERR_LAUNCH.
+ *
+ * idx_select_translate_planned - idx_select_translate with the row lengths
+ * taken from a plan: same outputs and guarantees, for rows of the lengths
+ * the plan was built from (row_len is not read).  It launches one workgroup
+ * per plan slot; slots past the plan's item count exit at once, and rows
+ * are never read past their length.  The plan must have been built on the
+ * same stream (or be ordered before this call) by topk_plan_rows with the
+ * same num_rows and max_len; a plan built from other lengths selects over
+ * those lengths (the kernel still stays inside every buffer).  workspace: at
+ * least topk_planned_workspace_bytes, zero-filled once (see above).
+ * Errors: as idx_select_translate, plus BS_ERR_NULL for a NULL plan and
+ * BS_ERR_WORKSPACE for plan_bytes < topk_plan_bytes(num_rows, max_len).
+ */
+size_t topk_plan_bytes(int32_t num_rows, int32_t max_len);
+size_t topk_planned_workspace_bytes(int32_t num_rows, int32_t max_len, int32_t k);
+int topk_plan_rows(const int32_t* row_len, int32_t num_rows, int32_t max_len, int32_t* plan, size_t plan_bytes,
+                   void* stream);
+int idx_select_translate_planned(const float* scores, int64_t ld_scores, int32_t num_rows, int32_t max_len,
+                                 int32_t k, const int32_t* req_row_ptr, int32_t num_req, const int32_t* row_pos,
+                                 int32_t c, const int32_t* page_table, int32_t pt_stride,
+                                 int32_t* sel, int32_t* sel_count,
+                                 int32_t* out_slots, int32_t* out_pos, int32_t* out_count, int32_t ld_out,
+                                 const int32_t* plan, size_t plan_bytes,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * idx_compress_store - compression of new raw index keys into the c = 4 key

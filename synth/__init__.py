@@ -43,6 +43,7 @@ SEEDS = {
     "qsa_indexshare_64req": 1006,
     "qsa_compress_prefill_8k": 1007,
     "qsa_compress_decode_64req": 1008,
+    "select_mixed_300rows": 1009,
 }
 
 # Rotary parameters of the compressed index key.  The pages name an MRoPE
@@ -115,6 +116,29 @@ class ScoreRows:
     scores: np.ndarray          # float32 [R][ld]
     row_len: np.ndarray         # int32 [R]
     seed: int
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.scores.shape[0])
+
+    @property
+    def max_len(self) -> int:
+        return int(self.scores.shape[1])
+
+
+@dataclasses.dataclass
+class SelectBatch:
+    """Given FP32 score rows of a paged batch, for the fused selection and
+    translation on its own (nothing is scored: `inp` carries the paging,
+    with zero queries and keys)."""
+
+    inp: "IndexerInputs"
+    scores: np.ndarray          # float32 [R][max_len]
+    row_len: np.ndarray         # int32 [R]
+
+    @property
+    def name(self) -> str:
+        return self.inp.name
 
     @property
     def num_rows(self) -> int:
@@ -401,6 +425,40 @@ def qsa_compress_decode_64req(seed: int = SEEDS["qsa_compress_decode_64req"], B:
                                 text_positions=True, rng=rng)
 
 
+def given_rows_batch(rng: np.random.Generator, ctx, c: int, k: int, row_pos=None,
+                     name: str = "given") -> IndexerInputs:
+    """A paged batch of one row per request (positions row_pos, default the
+    last context token) for selection on given FP32 rows: a seeded page
+    permutation, no keys (nothing is scored)."""
+    pages = [max(1, -(-t // 64)) for t in ctx]
+    perm = rng.permutation(int(sum(pages)))
+    pt = np.full((len(ctx), max(pages)), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        pt[b, :n] = perm[off:off + n]
+        off += n
+    t = np.array([x - 1 for x in ctx] if row_pos is None else row_pos, dtype=np.int32)
+    R = t.size
+    return IndexerInputs(name=name, c=c, k=k, q=np.zeros((R, 4, 128), np.uint16),
+                         kcache=np.zeros((64 // c, 128), np.uint16), num_pages=int(off), page_table=pt,
+                         req_row_ptr=np.arange(R + 1, dtype=np.int32), row_pos=t,
+                         max_vis=int(((t.astype(np.int64) + 1) // c).max()), seed=0)
+
+
+def select_mixed_300rows(seed: int = SEEDS["select_mixed_300rows"], R: int = 300, n_long: int = 16,
+                         L: int = 81920, k: int = 2048) -> SelectBatch:
+    """A mixed decode batch for the selection alone: 300 rows (one per
+    request, c = 1), 16 of them at 81,920 entries and the rest uniform in
+    2,000-8,000; FP32 scores ~N(0,1); top-2048 translated through 64-token
+    pages."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(2000, 8001, R).astype(np.int32)
+    lens[rng.choice(R, n_long, replace=False)] = L
+    inp = given_rows_batch(rng, [int(n) + 1 for n in lens], 1, k, name="select_mixed_300rows")
+    x = _normal_f32(rng, (R, L))
+    return SelectBatch(inp=inp, scores=x, row_len=lens)
+
+
 WORKLOADS = {
     "qsa_decode_1x8k": qsa_decode_1x8k,
     "topk_8x80k": topk_8x80k,
@@ -410,6 +468,7 @@ WORKLOADS = {
     "qsa_indexshare_64req": qsa_indexshare_64req,
     "qsa_compress_prefill_8k": qsa_compress_prefill_8k,
     "qsa_compress_decode_64req": qsa_compress_decode_64req,
+    "select_mixed_300rows": select_mixed_300rows,
 }
 
 

@@ -251,3 +251,64 @@ def test_noalloc_validation():
     too_many = bst.NOALLOC_SCRATCH_BYTES // per_row + 1
     assert _noalloc(num_rows=too_many) == BS_ERR_WORKSPACE
     assert "static scratch" in bst.status_string(BS_ERR_WORKSPACE)
+
+
+def test_plan_sizes():
+    assert bst.topk_plan_bytes(0, 81920) == 0
+    # one 16-byte slot per row below 16,385 entries, one per 8,192-entry chunk from there on
+    assert bst.topk_plan_bytes(300, 8192) == 32 + 16 * 300
+    assert bst.topk_plan_bytes(300, 16384) == 32 + 16 * 300
+    assert bst.topk_plan_bytes(300, 16385) == 32 + 16 * 300 * 3
+    assert bst.topk_plan_bytes(300, 81920) == 32 + 16 * 300 * 10
+    assert bst.topk_planned_workspace_bytes(300, 16384, 2048) == 0
+    w = bst.topk_planned_workspace_bytes(8, 20000, 2048)
+    assert w > 0 and w % (64 << 10) == 0
+    assert bst.topk_planned_workspace_bytes(16, 20000, 2048) == 2 * w
+    # records sized for rows split from 16,385 entries on cover the unplanned launch's
+    assert bst.topk_planned_workspace_bytes(16, 81920, 2048) >= bst.topk_workspace_bytes(16, 81920, 2048)
+
+
+def _plan(**kw):
+    a = dict(row_len=FAKE, num_rows=300, max_len=81920, plan=FAKE, plan_bytes=32 + 16 * 3000, stream=NULL)
+    a.update(kw)
+    return bst.lib().topk_plan_rows(a["row_len"], a["num_rows"], a["max_len"], a["plan"], a["plan_bytes"],
+                                    a["stream"])
+
+
+def _planned(**kw):
+    a = dict(scores=FAKE, ld=81920, num_rows=300, max_len=81920, k=2048, ptr=FAKE, num_req=300, pos=FAKE, c=1,
+             pt=FAKE, pt_stride=1280, sel=FAKE, cnt=FAKE, slots=FAKE, opos=NULL, ocnt=FAKE, ld_out=2048, plan=FAKE,
+             plan_bytes=32 + 16 * 3000, ws=FAKE, ws_bytes=0, stream=NULL)
+    a.update(kw)
+    return bst.lib().idx_select_translate_planned(a["scores"], a["ld"], a["num_rows"], a["max_len"], a["k"],
+                                                  a["ptr"], a["num_req"], a["pos"], a["c"], a["pt"], a["pt_stride"],
+                                                  a["sel"], a["cnt"], a["slots"], a["opos"], a["ocnt"], a["ld_out"],
+                                                  a["plan"], a["plan_bytes"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_plan_validation():
+    # host-side checks only: every case fails (or is a no-op) before anything is launched
+    assert _plan(num_rows=0) == BS_OK
+    assert _plan(num_rows=-1) == BS_ERR_ARG
+    assert _plan(max_len=-1) == BS_ERR_ARG
+    assert _plan(max_len=65535 * 4096 + 1, num_rows=1, plan_bytes=1 << 40) == BS_ERR_ARG
+    assert _plan(num_rows=(1 << 22) // 10 + 1, plan_bytes=1 << 40) == BS_ERR_ARG  # more than 2^22 slots
+    assert _plan(row_len=NULL) == BS_ERR_NULL
+    assert _plan(plan=NULL) == BS_ERR_NULL
+    assert _plan(plan_bytes=32 + 16 * 3000 - 1) == BS_ERR_WORKSPACE
+
+
+def test_planned_select_validation():
+    need = bst.topk_planned_workspace_bytes(300, 81920, 2048)
+    assert _planned(num_rows=0) == BS_OK
+    assert _planned(k=0, ws_bytes=need) == BS_ERR_ARG
+    assert _planned(k=2049, ws_bytes=need) == BS_ERR_ARG
+    assert _planned(c=2, ws_bytes=need) == BS_ERR_ARG
+    assert _planned(ld_out=2047, ws_bytes=need) == BS_ERR_ARG
+    assert _planned(ld=81919, ws_bytes=need) == BS_ERR_ARG
+    assert _planned(num_req=0, ws_bytes=need) == BS_ERR_ARG
+    for k in ("scores", "plan", "sel", "cnt", "ptr", "pos", "pt", "slots", "ocnt"):
+        assert _planned(**{k: NULL}, ws_bytes=need) == BS_ERR_NULL, k
+    assert _planned(plan_bytes=32 + 16 * 3000 - 1, ws_bytes=need) == BS_ERR_WORKSPACE
+    assert _planned(ws_bytes=need - 1) == BS_ERR_WORKSPACE
+    assert _planned(ws=NULL, ws_bytes=need) == BS_ERR_WORKSPACE

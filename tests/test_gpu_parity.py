@@ -535,22 +535,7 @@ def test_fused_select_translate_on_given_rows():
 
 
 def _given_rows_batch(rng, ctx, c, k, row_pos=None):
-    """A paged batch of one row per request (positions row_pos, default the
-    last context token) for selection on given FP32 rows: a seeded page
-    permutation, no keys (nothing is scored)."""
-    pages = [max(1, -(-t // 64)) for t in ctx]
-    perm = rng.permutation(int(sum(pages)))
-    pt = np.full((len(ctx), max(pages)), -1, dtype=np.int32)
-    off = 0
-    for b, n in enumerate(pages):
-        pt[b, :n] = perm[off:off + n]
-        off += n
-    t = np.array([x - 1 for x in ctx] if row_pos is None else row_pos, dtype=np.int32)
-    R = t.size
-    return synth.IndexerInputs(name="given", c=c, k=k, q=np.zeros((R, 4, 128), np.uint16),
-                               kcache=np.zeros((64 // c, 128), np.uint16), num_pages=int(off), page_table=pt,
-                               req_row_ptr=np.arange(R + 1, dtype=np.int32), row_pos=t,
-                               max_vis=int(((t.astype(np.int64) + 1) // c).max()), seed=0)
+    return synth.given_rows_batch(rng, ctx, c, k, row_pos)
 
 
 def _select_translate_given(inp, rows, lens, max_len, reps=1):
@@ -613,7 +598,7 @@ def test_fused_many_rows_exact(c):
 
 @pytest.mark.parametrize("c", [1, 4])
 def test_long_rows_fused_exact(c):
-    # rows of >= 32,769 entries (one workgroup per 16,384-entry chunk, the last
+    # rows of >= 32,769 entries (one workgroup per 8,192-entry chunk, the last
     # to arrive resolving the row): random rows (candidate filter), tie storms
     # and a row whose winners sit in one chunk (the whole-row fallback), row
     # lengths that are not a multiple of the chunk, 3 calls on one workspace.
@@ -677,6 +662,145 @@ def test_mixed_batch_long_rows_among_many():
     inp = _given_rows_batch(rng, [int(n) for n in lens], c, k)
     rows = rng.standard_normal((R, 81920)).astype(np.float32)
     _check_given(inp, rows, lens, _select_translate_given(inp, rows, lens, 81920, reps=2))
+
+
+def _items_of(lens, cut):
+    return int(sum(-(-int(n) // 8192) if n >= cut else 1 for n in lens))
+
+
+def _planned_given(inp, rows, lens, max_len, ks=None, reps=2):
+    """topk_plan_rows once, then idx_select_translate_planned on that plan
+    `reps` times for each k in ks (default inp.k), one workspace sized for the
+    largest k; returns the plan's header and [(inp for that k, outputs)]."""
+    import dataclasses
+    import block_scoring_top_amd as bst
+    from synth.device import upload
+    dev = upload(inp, "cuda")
+    R = inp.num_rows
+    ks = ks or [inp.k]
+    s = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.float32)).cuda()
+    rl = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+    plan = bst.topk_plan(R, max_len, "cuda")
+    ws = bst.topk_planned_workspace(R, max_len, max(ks), "cuda")
+    gu.say(f"plan rows={R} max_len={max_len}")
+    bst.topk_plan_rows(rl, max_len, plan)
+    rl.fill_(-5)  # the selection must take the lengths from the plan
+    torch.cuda.synchronize()
+    header = plan[:8].cpu().numpy()
+    outs = []
+    for k in ks:
+        ik = dataclasses.replace(inp, k=k)
+        for rep in range(reps):
+            gu.say(f"planned select_translate rows={R} max_len={max_len} k={k} c={inp.c} rep={rep}")
+            sel = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+            cnt = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+            slots = torch.full((R, ik.ld_out), -7, dtype=torch.int32, device="cuda")
+            pos = torch.full((R, ik.ld_out), -7, dtype=torch.int32, device="cuda")
+            oc = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+            bst.idx_select_translate_planned(s, max_len, k, dev.req_row_ptr, dev.row_pos, inp.c, dev.page_table,
+                                             sel, cnt, slots, oc, plan, out_pos=pos, workspace=ws)
+            torch.cuda.synchronize()
+            outs.append((ik, tuple(t.cpu().numpy() for t in (sel, cnt, slots, pos, oc))))
+            if ws is not None:
+                assert _ws_clean(ws), "the first word of every 64 KiB block of the workspace must be left zero"
+    return header, outs
+
+
+def _check_planned(rows, lens, max_len, header, outs):
+    assert header[2] == len(lens) and header[3] == max_len
+    cut = int(header[1])
+    assert cut in (16385, 32769)
+    n = np.minimum(lens, max_len)
+    assert int(header[0]) == _items_of(n, cut)
+    assert int(header[4]) == int(sum(-(-int(x) // 8192) for x in n if x >= cut))  # the chunk items, listed first
+    for ik, o in outs:
+        _check_given(ik, rows, lens, [o])
+    return cut
+
+
+@pytest.mark.parametrize("c", [1, 4])
+def test_planned_mixed_batch_exact(c):
+    # 300 rows, 16 of them at 81,920 entries and the rest at 2,000-8,000: the
+    # plan is built once and serves two selections; each long row is split
+    # into 10 chunk items and every other row is one whole-row item, read
+    # only up to its length.
+    rng = np.random.default_rng(1600 + c)
+    R = 300
+    k = 2048 if c == 1 else 512
+    lens = rng.integers(2000, 8001, R).astype(np.int32)
+    lens[rng.choice(R, 16, replace=False)] = 81920
+    ctx = [int(c * (n + 1)) for n in lens]
+    inp = _given_rows_batch(rng, ctx, c, k)
+    rows = rng.standard_normal((R, 81920)).astype(np.float32)
+    rows[3] = synth.tie_storm_rows(1601, 4, 81920)[2]
+    header, outs = _planned_given(inp, rows, lens, 81920, reps=2)
+    _check_planned(rows, lens, 81920, header, outs)
+
+
+def test_planned_plan_reused_across_k():
+    # One plan (it depends on the lengths only) serving selections with
+    # different k, as the layers of one step would; one workspace sized for
+    # the largest k.
+    rng = np.random.default_rng(1700)
+    c = 4
+    lens = np.array([81920, 40000, 32769, 20000, 16385, 16384, 9000, 8192, 2048, 100, 1, 0], dtype=np.int32)
+    ctx = [int(c * (n + 1)) for n in lens]
+    inp = _given_rows_batch(rng, ctx, c, 512)
+    rows = rng.standard_normal((lens.size, 81920)).astype(np.float32)
+    rows[1, 30000:31000] += np.float32(4.0)  # winners clustered in one chunk (the whole-row fallback)
+    header, outs = _planned_given(inp, rows, lens, 81920, ks=[512, 2048, 64], reps=1)
+    cut = _check_planned(rows, lens, 81920, header, outs)
+    assert cut == 16385  # 12 rows fit on the device at once, so rows from 16,385 entries on are split
+
+
+def test_planned_many_rows_keep_medium_rows_whole():
+    # More items at the low split length than the device holds at once: the
+    # plan splits only rows of 32,769 entries or more, and the 16,385-32,768
+    # rows are selected whole (streamed).
+    rng = np.random.default_rng(1800)
+    R, c, k = 1100, 1, 2048
+    lens = rng.integers(16385, 32769, R).astype(np.int32)
+    lens[:4] = [16385, 24576, 32768, 2]
+    lens[4:8] = [32769, 40000, 65536, 49152]
+    ctx = [int(c * (n + 1)) for n in lens]
+    inp = _given_rows_batch(rng, ctx, c, k)
+    rows = rng.standard_normal((R, 65536)).astype(np.float32)
+    rows[8:16] = synth.tie_storm_rows(1801, 8, 65536)
+    header, outs = _planned_given(inp, rows, lens, 65536, reps=1)
+    assert _check_planned(rows, lens, 65536, header, outs) == 32769
+
+
+def test_planned_rows_past_the_register_blocks():
+    # 5,000 rows: the planner keeps 4,096 rows' lengths in registers between
+    # its passes and reads the rest again; many rows, so only rows of 32,769
+    # entries or more are split (three here, in the middle of the batch).
+    rng = np.random.default_rng(2000)
+    R, c, k = 5000, 1, 256
+    lens = rng.integers(0, 3001, R).astype(np.int32)
+    lens[[0, 2500, 4500]] = [40000, 32769, 36000]
+    lens[4096:4100] = [0, 1, 256, 257]
+    ctx = [int(c * (n + 1)) for n in lens]
+    inp = _given_rows_batch(rng, ctx, c, k)
+    rows = np.zeros((R, 40000), dtype=np.float32)
+    for r in np.flatnonzero(lens):
+        rows[r, :lens[r]] = rng.standard_normal(int(lens[r])).astype(np.float32)
+    header, outs = _planned_given(inp, rows, lens, 40000, reps=1)
+    assert _check_planned(rows, lens, 40000, header, outs) == 32769
+
+
+def test_planned_short_rows_only():
+    # max_len below 16,385: no workspace, one whole-row item per row, every
+    # length edge (0, 1, k - 1, k, k + 1, a full register tile, past it).
+    rng = np.random.default_rng(1900)
+    c, k = 1, 512
+    lens = np.array([0, 1, 511, 512, 513, 8192, 8193, 12000, 16384] + [3000] * 40, dtype=np.int32)
+    ctx = [int(c * (n + 1)) for n in lens]
+    inp = _given_rows_batch(rng, ctx, c, k)
+    rows = rng.standard_normal((lens.size, 16384)).astype(np.float32)
+    rows[9:20] = synth.tie_storm_rows(1901, 11, 16384)
+    header, outs = _planned_given(inp, rows, lens, 16384, reps=2)
+    _check_planned(rows, lens, 16384, header, outs)
+    assert int(header[0]) == lens.size
 
 
 # ---------------------------------------------------------------------------
