@@ -9,7 +9,8 @@ from __future__ import annotations
 import torch
 
 from . import (idx_expand_translate, idx_score_decode, idx_score_prefill, idx_select_translate,
-               prepare_score, prepare_select_translate, topk_select_rows, topk_workspace)
+               idx_select_translate_planned, prepare_score, prepare_select_translate, topk_plan, topk_plan_rows,
+               topk_planned_workspace, topk_select_rows, topk_workspace)
 
 
 class IndexerPath:
@@ -38,6 +39,8 @@ class IndexerPath:
         self.pos = torch.empty((R, ld_out), dtype=torch.int32, device=dev)
         self.out_count = torch.empty(R, dtype=torch.int32, device=dev)
         self.workspace = topk_workspace(R, int(inp.max_vis), inp.k, dev)
+        self.plan_buf = None          # planned selection: allocated on first use
+        self.planned_workspace = None
         self._prepared = None
 
     def _prepare(self):
@@ -74,6 +77,26 @@ class IndexerPath:
                              i.page_table, self.sel, self.sel_count, self.slots, self.out_count, out_pos=self.pos,
                              workspace=self.workspace, stream=stream)
 
+    def plan(self, stream=None):
+        """Builds the selection's work list from ``row_len`` (as the scorer
+        wrote it); every later ``select_translate_planned`` uses it, until the
+        next call here (the lengths change only with the row positions)."""
+        i = self.inp
+        if self.plan_buf is None:
+            R, dev = int(i.row_pos.shape[0]), i.q.device
+            self.plan_buf = topk_plan(R, int(i.max_vis), dev)
+            self.planned_workspace = topk_planned_workspace(R, int(i.max_vis), i.k, dev)
+        topk_plan_rows(self.row_len, int(i.max_vis), self.plan_buf, stream=stream)
+
+    def select_translate_planned(self, stream=None):
+        """``select_translate`` over the work list of the last ``plan``."""
+        if self.plan_buf is None:
+            raise RuntimeError("plan() must be called first")
+        i = self.inp
+        idx_select_translate_planned(self.scores, int(i.max_vis), i.k, i.req_row_ptr, i.row_pos, i.c, i.page_table,
+                                     self.sel, self.sel_count, self.slots, self.out_count, self.plan_buf,
+                                     out_pos=self.pos, workspace=self.planned_workspace, stream=stream)
+
     def prepared(self):
         """(score, select_translate) as prepared calls: each takes an optional
         stream and launches with no per-call argument checking."""
@@ -81,10 +104,15 @@ class IndexerPath:
             self._prepare()
         return self._prepared
 
-    def run(self, stream=None, fused: bool = True):
+    def run(self, stream=None, fused: bool = True, planned: bool = False):
         """One pass of the path: score, then select + translate (fused into one
-        kernel, the default) or the separate select and expand calls."""
-        if fused:
+        kernel, the default) or the separate select and expand calls.
+        planned: score, plan, then the planned select + translate."""
+        if planned:
+            self.score(stream)
+            self.plan(stream)
+            self.select_translate_planned(stream)
+        elif fused:
             score, select_translate = self.prepared()
             score(stream)
             select_translate(stream)

@@ -17,12 +17,12 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def run_path(inp, scorer: str = "decode", fused: bool = True):
-    say(f"path {scorer} fused={fused}: {getattr(inp, 'name', '?')} rows={inp.num_rows} max_vis={inp.max_vis} "
-        f"k={inp.k} c={inp.c}")
+def run_path(inp, scorer: str = "decode", fused: bool = True, planned: bool = False):
+    say(f"path {scorer} fused={fused} planned={planned}: {getattr(inp, 'name', '?')} rows={inp.num_rows} "
+        f"max_vis={inp.max_vis} k={inp.k} c={inp.c}")
     dev = upload(inp, "cuda")
     p = IndexerPath(dev, scorer)
-    p.run(fused=fused)
+    p.run(fused=fused, planned=planned)
     torch.cuda.synchronize()
     return dict(scores=p.scores.cpu().numpy(), row_len=p.row_len.cpu().numpy(), sel=p.sel.cpu().numpy(),
                 sel_count=p.sel_count.cpu().numpy(), slots=p.slots.cpu().numpy(), pos=p.pos.cpu().numpy(),

@@ -20,11 +20,12 @@ pytestmark = pytest.mark.gpu
 gu = pytest.importorskip("gpu_util")
 
 
-def _full_check(inp, scorer="decode", fused=True):
+def _full_check(inp, scorer="decode", fused=True, planned=False):
     """Every stage against the oracle: scores (tolerance), top-k of the GPU
     scores (exact), end-to-end selection (band), expand of the GPU selection
-    (exact).  fused: select + translate in one kernel, else separate calls."""
-    g = gu.run_path(inp, scorer, fused)
+    (exact).  fused: select + translate in one kernel, else separate calls;
+    planned: the selection over a plan built from the scorer's row lengths."""
+    g = gu.run_path(inp, scorer, fused, planned)
     ref = oracle.pipeline(inp)
     assert np.array_equal(g["row_len"], ref["row_len"])
     check_scores(g["scores"], ref["scores"], ref["row_len"])
@@ -126,6 +127,16 @@ def test_decode_power_of_two_scaling_exact():
     for r in range(inp.num_rows):
         n = l1[r]
         assert np.array_equal(s2[r, :n], np.float32(2.0) * s1[r, :n])
+
+
+@pytest.mark.parametrize("wl", ["verify", "dsa"])
+def test_decode_planned_end_to_end(wl):
+    # score -> plan (from the scorer's row lengths) -> planned select+translate:
+    # the ragged verify batch (rows of 75-5,000 blocks) and long DSA rows
+    # (split into chunk items).
+    inp = (synth.qsa_verify_64req(B=8, lo=300, hi=20000) if wl == "verify"
+           else synth.dsa_decode_16x80k(B=3, L=40000))
+    _full_check(inp, planned=True)
 
 
 def test_decode_leaves_invisible_entries_untouched():
