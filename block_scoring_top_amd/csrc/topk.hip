@@ -961,6 +961,11 @@ __global__ __launch_bounds__(NT, NT == kManyNT ? 4 : NT == kMidNT ? 2 : 1) void 
                                                           sel + (int64_t)r * k, sel_count, r, tr);
 }
 
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
+
 // Long rows, one launch.  Every workgroup holds the row kernels' shared
 // memory (histogram, boundary list, selection, a page cache sized for long
 // rows).
@@ -1056,7 +1061,7 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
                                            int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
                                            uint8_t* __restrict__ ws, int64_t rec_bytes, int32_t wmax,
                                            const Translate& tr) {
-  constexpr int VPT = kCkVpt, CH = NT * VPT, B = kBins / NT, P = VPT / 2, PA = kCkAll / NT;
+  constexpr int VPT = kCkVpt, CH = NT * VPT, B = kBins / NT, P = VPT / 2;
   static_assert(B == 2, "the published histogram packs each lane's two bins into one 32-bit store");
   static_assert(CH <= 65535, "a chunk's per-bin counts fit 16 bits");
   TopkShared<kCkCand, kCkPages>& s = cs.t;
@@ -1174,105 +1179,116 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
   // ---- Resolution (the last chunk to arrive) ----
   const int nall = nchunk * Q;
   const bool fits = nall <= kCkAll && nchunk <= kCkMeta;
-  RowPagePrefetch<NT, TRANSLATE, kCkPages> pf{tr, r, gr};
-  uint64_t v[PA];
-  uint32_t hs[B];
-#pragma unroll
-  for (int i = 0; i < B; ++i) hs[i] = 0;
-  // Every load below is unconditional, through buffer resources covering
-  // just the valid range (lanes past it read 0 without a memory access), and
-  // masked once it has arrived: a load under a condition ends in a wait at
-  // the branch join, which would serialise the round trips.
-  const uint32_t vmeta = fits ? (uint32_t)nchunk * 4u : 0u, vcand = fits ? (uint32_t)nall * 8u : 0u;
-  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(meta, (short)0, vmeta, 0x00020000);
-  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(gcand, (short)0, vcand, 0x00020000);
-  const __amdgpu_buffer_rsrc_t hrs =
-      __builtin_amdgcn_make_buffer_rsrc(ghist, (short)0, fits ? (uint32_t)nchunk * kBins * 2u : 0u, 0x00020000);
-  const uint32_t mt = ws_buffer_load32(mrs, (uint32_t)tid * 4u);
-#pragma unroll
-  for (int p = 0; p < PA; ++p) v[p] = ws_buffer_load64(grs, (uint32_t)(p * NT + tid) * 8u);
-  // The union's histogram: the sum of the chunks' published histograms
-  // (one packed load per chunk per lane), 32 chunks' loads in flight at a
-  // time (one round trip up to 32 chunks).
-  for (int c0 = 0; c0 < (fits ? nchunk : 0); c0 += 32) {
-    uint32_t h[32];
-#pragma unroll
-    for (int u = 0; u < 32; ++u)
-      h[u] = ws_buffer_load32(hrs, ((uint32_t)(c0 + u) * (kBins / 2) + (uint32_t)(kBins / 2 - 1 - tid)) * 4u);
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      hs[0] += h[u] >> 16;
-      hs[1] += h[u] & 0xFFFFu;
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < PA; ++p) v[p] = p * NT + tid < nall ? v[p] : kNoCand;
-  pf.issue();
-  if (tid < nchunk) atomicMax(&s.bmax, mt & 0xFFFFu);
-  if (tid == 0) s.emit = 0;
-  pf.commit(s);
-  __syncthreads();
-  uint32_t T = 0, above = 0, inT = 0;
-  block_threshold<NT>(s, hs, (uint32_t)k, T, above, inT);
-  const bool fast = fits && T >= s.bmax;
-  if (fast) {
-    // Code per slot: bin + 1 for a candidate, 0 for an unused slot.
-    uint32_t code[PA];
-#pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      const uint32_t b = bin_of(__uint_as_float((uint32_t)(v[p] >> 32))) + 1u;
-      code[p] = v[p] != kNoCand ? b : 0u;
-    }
-    // Above T: the selection (LDS); in T: the boundary list as composite
-    // keys.  Positions: one packed (above << 16 | in-bin) reservation per
-    // wave.  Every slot writes both lists, the ones it does not belong to at
-    // this lane's own scratch entries (no branch per slot).
-    const uint32_t t1 = T + 1u;
-    uint32_t upm = 0, eqm = 0;
-#pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      upm |= (code[p] > t1 ? 1u : 0u) << p;
-      eqm |= (code[p] == t1 ? 1u : 0u) << p;
-    }
-    const uint32_t base =
-        wave_reserve_n(&s.emit, ((uint32_t)__builtin_popcount(upm) << 16) | (uint32_t)__builtin_popcount(eqm));
-    uint32_t pu = base >> 16, pe = base & 0xFFFFu;
-#pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      const uint32_t up = (upm >> p) & 1u, eq = (eqm >> p) & 1u;
-      int32_t* du = up && pu < (uint32_t)k ? &s.chosen[pu] : &cs.trash32[tid];
-      uint64_t* de = eq && pe < (uint32_t)kCkCand ? &s.cand[pe] : &cs.trash64[tid];
-      *du = (int)(uint32_t)v[p];
-      *de = composite_key(__uint_as_float((uint32_t)(v[p] >> 32)), (int)(uint32_t)v[p]);
-      pu += up;
-      pe += eq;
-    }
-    __syncthreads();
-    const uint32_t nc = s.emit & 0xFFFFu, need = (uint32_t)k - above;
-    if (need >= 1 && need <= (uint32_t)k) {
-      if (nc <= (uint32_t)kCkCand) {
-        if (need >= nc) {
-          for (uint32_t i = tid; i < nc; i += NT) s.chosen[above + i] = index_of(s.cand[i]);
-        } else if (nc <= (uint32_t)kRankMax) {
-          rank_refine<NT>(s, nc, need, nullptr, s.chosen, above);
-        } else {
-          block_refine<NT>(s, nc, need, nullptr, s.chosen, above, k);
-        }
-        __syncthreads();
-      } else {
-        if (tid == 0) s.emit = above;
-        __syncthreads();
-        block_refine_from_row<NT>(s, row, n, T, need, nullptr, s.chosen, k);
+  // The candidates are held PA per lane: 8 when they fit (most rows), else
+  // 16.  Two copies of the resolution, so that the common one carries half
+  // the registers and instructions (its code is cold on the compute unit
+  // that resolves, so its length costs time too).
+  auto resolve = [&](auto pa_tag) __attribute__((always_inline)) {
+    constexpr int PA = decltype(pa_tag)::value;
+    RowPagePrefetch<NT, TRANSLATE, kCkPages> pf{tr, r, gr};
+    uint64_t v[PA];
+    uint32_t hs[B];
+  #pragma unroll
+    for (int i = 0; i < B; ++i) hs[i] = 0;
+    // Every load below is unconditional, through buffer resources covering
+    // just the valid range (lanes past it read 0 without a memory access), and
+    // masked once it has arrived: a load under a condition ends in a wait at
+    // the branch join, which would serialise the round trips.
+    const uint32_t vmeta = fits ? (uint32_t)nchunk * 4u : 0u, vcand = fits ? (uint32_t)nall * 8u : 0u;
+    const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(meta, (short)0, vmeta, 0x00020000);
+    const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(gcand, (short)0, vcand, 0x00020000);
+    const __amdgpu_buffer_rsrc_t hrs =
+        __builtin_amdgcn_make_buffer_rsrc(ghist, (short)0, fits ? (uint32_t)nchunk * kBins * 2u : 0u, 0x00020000);
+    const uint32_t mt = ws_buffer_load32(mrs, (uint32_t)tid * 4u);
+  #pragma unroll
+    for (int p = 0; p < PA; ++p) v[p] = ws_buffer_load64(grs, (uint32_t)(p * NT + tid) * 8u);
+    // The union's histogram: the sum of the chunks' published histograms
+    // (one packed load per chunk per lane), 32 chunks' loads in flight at a
+    // time (one round trip up to 32 chunks).
+    for (int c0 = 0; c0 < (fits ? nchunk : 0); c0 += 32) {
+      uint32_t h[32];
+  #pragma unroll
+      for (int u = 0; u < 32; ++u)
+        h[u] = ws_buffer_load32(hrs, ((uint32_t)(c0 + u) * (kBins / 2) + (uint32_t)(kBins / 2 - 1 - tid)) * 4u);
+  #pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        hs[0] += h[u] >> 16;
+        hs[1] += h[u] & 0xFFFFu;
       }
     }
-    for (int i = tid; i < k; i += NT) out[i] = s.chosen[i];
-    if (tid == 0) sel_count[r] = k;
-    if (TRANSLATE) translate_row<NT>(tr, pf.g, r, k, s.chosen, s.row_pages, (int)s.row_npages);
-  } else {
-    // Some chunk held more of the row's top than its quota: select the whole
-    // row here, streaming it (exact; rare on unclustered rows).
-    select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, k, k, out, sel_count, r, tr);
-  }
+  #pragma unroll
+    for (int p = 0; p < PA; ++p) v[p] = p * NT + tid < nall ? v[p] : kNoCand;
+    pf.issue();
+    if (tid < nchunk) atomicMax(&s.bmax, mt & 0xFFFFu);
+    if (tid == 0) s.emit = 0;
+    pf.commit(s);
+    __syncthreads();
+    uint32_t T = 0, above = 0, inT = 0;
+    block_threshold<NT>(s, hs, (uint32_t)k, T, above, inT);
+    const bool fast = fits && T >= s.bmax;
+    if (fast) {
+      // Code per slot: bin + 1 for a candidate, 0 for an unused slot.
+      uint32_t code[PA];
+  #pragma unroll
+      for (int p = 0; p < PA; ++p) {
+        const uint32_t b = bin_of(__uint_as_float((uint32_t)(v[p] >> 32))) + 1u;
+        code[p] = v[p] != kNoCand ? b : 0u;
+      }
+      // Above T: the selection (LDS); in T: the boundary list as composite
+      // keys.  Positions: one packed (above << 16 | in-bin) reservation per
+      // wave.  Every slot writes both lists, the ones it does not belong to at
+      // this lane's own scratch entries (no branch per slot).
+      const uint32_t t1 = T + 1u;
+      uint32_t upm = 0, eqm = 0;
+  #pragma unroll
+      for (int p = 0; p < PA; ++p) {
+        upm |= (code[p] > t1 ? 1u : 0u) << p;
+        eqm |= (code[p] == t1 ? 1u : 0u) << p;
+      }
+      const uint32_t base =
+          wave_reserve_n(&s.emit, ((uint32_t)__builtin_popcount(upm) << 16) | (uint32_t)__builtin_popcount(eqm));
+      uint32_t pu = base >> 16, pe = base & 0xFFFFu;
+  #pragma unroll
+      for (int p = 0; p < PA; ++p) {
+        const uint32_t up = (upm >> p) & 1u, eq = (eqm >> p) & 1u;
+        int32_t* du = up && pu < (uint32_t)k ? &s.chosen[pu] : &cs.trash32[tid];
+        uint64_t* de = eq && pe < (uint32_t)kCkCand ? &s.cand[pe] : &cs.trash64[tid];
+        *du = (int)(uint32_t)v[p];
+        *de = composite_key(__uint_as_float((uint32_t)(v[p] >> 32)), (int)(uint32_t)v[p]);
+        pu += up;
+        pe += eq;
+      }
+      __syncthreads();
+      const uint32_t nc = s.emit & 0xFFFFu, need = (uint32_t)k - above;
+      if (need >= 1 && need <= (uint32_t)k) {
+        if (nc <= (uint32_t)kCkCand) {
+          if (need >= nc) {
+            for (uint32_t i = tid; i < nc; i += NT) s.chosen[above + i] = index_of(s.cand[i]);
+          } else if (nc <= (uint32_t)kRankMax) {
+            rank_refine<NT>(s, nc, need, nullptr, s.chosen, above);
+          } else {
+            block_refine<NT>(s, nc, need, nullptr, s.chosen, above, k);
+          }
+          __syncthreads();
+        } else {
+          if (tid == 0) s.emit = above;
+          __syncthreads();
+          block_refine_from_row<NT>(s, row, n, T, need, nullptr, s.chosen, k);
+        }
+      }
+      for (int i = tid; i < k; i += NT) out[i] = s.chosen[i];
+      if (tid == 0) sel_count[r] = k;
+      if (TRANSLATE) translate_row<NT>(tr, pf.g, r, k, s.chosen, s.row_pages, (int)s.row_npages);
+    } else {
+      // Some chunk held more of the row's top than its quota: select the whole
+      // row here, streaming it (exact; rare on unclustered rows).
+      select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, k, k, out, sel_count, r, tr);
+    }
+  };
+  if (nall <= 8 * NT)
+    resolve(IntTag<8>{});
+  else
+    resolve(IntTag<kCkAll / NT>{});
   // Leave the first word of every kWsBlock-byte block of the row's record
   // zero: every layout a later call may lay over the workspace (other row
   // counts, lengths, k) puts its row counters on such words, and everything
