@@ -143,6 +143,7 @@ struct TopkShared {
   uint32_t bmax;
   uint32_t inbin;
   uint64_t red_and[16], red_or[16];
+  uint32_t out_ctr;       // output positions handed out by the boundary refinement
   int32_t row_pages[RP];  // page ids 0 .. row_npages-1 of a whole row's request (fused translation)
   uint32_t row_npages;
 };
@@ -280,9 +281,17 @@ __device__ __forceinline__ uint32_t block_excl_scan(TopkShared<CAP, RP>& s, uint
 // every wave finds the same digit from that histogram by itself.  Three digit
 // buffers rotate (in s.hist, free once the threshold bin is known), so one
 // barrier per pass suffices: the buffer pass p + 1 fills was last read in
-// pass p - 2 and is cleared during pass p.  The `need` winners are
-// emitted by count, block scan, write at out[base ...] (and chosen[base ...]).
-template <int NT, int CAP, int RP, int PER>
+// pass p - 2 and is cleared during pass p.  The `need` winners are written
+// at out[base ...] (and chosen[base ...]) in an unspecified order, each wave
+// taking its positions with one LDS atomic.
+// AO: the caller has already published (before a barrier) s.red_and[0] and
+// s.red_or[0], zeroed digit buffers 0 and 1 (s.hist[0 .. 512)) and
+// s.out_ctr.  The two words are the AND and the OR of the nc keys, or any
+// pair whose highest differing bit is at or above the keys' own and on whose
+// bits above it every key agrees with them (the passes then start from a
+// higher bit).  Without AO the exact AND and OR are found here, at the cost
+// of one more barrier.
+template <int NT, int CAP, int RP, int PER, bool AO = false>
 __device__ __forceinline__ void block_refine_per(TopkShared<CAP, RP>& s, uint32_t nc, uint32_t need,
                                                  int32_t* __restrict__ out, int32_t* chosen, uint32_t base, int limit) {
   static_assert(3 * 256 <= kBins, "three digit buffers fit in the histogram's storage");
@@ -299,20 +308,26 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP, RP>& s, uint32_
       o |= key[i];
     }
   }
-  a = wave_and64(a);
-  o = wave_or64(o);
-  if (lane_id() == 0) {
-    s.red_and[wave] = a;
-    s.red_or[wave] = o;
-  }
-  for (int i = tid; i < 512; i += NT) dig[i] = 0;  // buffers 0 and 1
-  __syncthreads();
-  a = ~0ull;
-  o = 0ull;
+  if (AO) {
+    a = s.red_and[0];
+    o = s.red_or[0];
+  } else {
+    a = wave_and64(a);
+    o = wave_or64(o);
+    if (lane_id() == 0) {
+      s.red_and[wave] = a;
+      s.red_or[wave] = o;
+    }
+    for (int i = tid; i < 512; i += NT) dig[i] = 0;  // buffers 0 and 1
+    if (tid == 0) s.out_ctr = 0;
+    __syncthreads();
+    a = ~0ull;
+    o = 0ull;
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    a &= s.red_and[w];
-    o |= s.red_or[w];
+    for (int w = 0; w < NT / 64; ++w) {
+      a &= s.red_and[w];
+      o |= s.red_or[w];
+    }
   }
   const uint64_t diff = a ^ o;
   int hb = diff ? 63 - __clzll((long long)diff) : 0;
@@ -345,8 +360,7 @@ __device__ __forceinline__ void block_refine_per(TopkShared<CAP, RP>& s, uint32_
   uint32_t cnt = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) cnt += ((uint32_t)(i * NT + tid) < nc && (key[i] & mask) >= prefix) ? 1u : 0u;
-  uint32_t total;
-  uint32_t pos = base + block_excl_scan<NT>(s, cnt, total);
+  uint32_t pos = base + wave_reserve_n(&s.out_ctr, cnt);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if ((uint32_t)(i * NT + tid) < nc && (key[i] & mask) >= prefix) {
@@ -390,14 +404,14 @@ __device__ __forceinline__ void rank_refine(TopkShared<CAP, RP>& s, uint32_t nc,
   }
 }
 
-template <int NT, int CAP, int RP>
+template <int NT, int CAP, int RP, bool AO = false>
 __device__ __forceinline__ void block_refine(TopkShared<CAP, RP>& s, uint32_t nc, uint32_t need, int32_t* __restrict__ out,
                                              int32_t* chosen, uint32_t base, int limit) {
   constexpr int PMAX = (CAP + NT - 1) / NT;
-  if (PMAX > 1 && nc <= (uint32_t)NT) block_refine_per<NT, CAP, RP, 1>(s, nc, need, out, chosen, base, limit);
-  else if (PMAX > 2 && nc <= 2u * NT) block_refine_per<NT, CAP, RP, 2>(s, nc, need, out, chosen, base, limit);
-  else if (PMAX > 4 && nc <= 4u * NT) block_refine_per<NT, CAP, RP, 4>(s, nc, need, out, chosen, base, limit);
-  else block_refine_per<NT, CAP, RP, PMAX>(s, nc, need, out, chosen, base, limit);
+  if (PMAX > 1 && nc <= (uint32_t)NT) block_refine_per<NT, CAP, RP, 1, AO>(s, nc, need, out, chosen, base, limit);
+  else if (PMAX > 2 && nc <= 2u * NT) block_refine_per<NT, CAP, RP, 2, AO>(s, nc, need, out, chosen, base, limit);
+  else if (PMAX > 4 && nc <= 4u * NT) block_refine_per<NT, CAP, RP, 4, AO>(s, nc, need, out, chosen, base, limit);
+  else block_refine_per<NT, CAP, RP, PMAX, AO>(s, nc, need, out, chosen, base, limit);
 }
 
 // Block-wide fallback when the boundary bin overflows the LDS list: radix
@@ -1188,7 +1202,7 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
     RowPagePrefetch<NT, TRANSLATE, kCkPages> pf{tr, r, gr};
     uint64_t v[PA];
     uint32_t hs[B];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < B; ++i) hs[i] = 0;
     // Every load below is unconditional, through buffer resources covering
     // just the valid range (lanes past it read 0 without a memory access), and
@@ -1200,27 +1214,36 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
     const __amdgpu_buffer_rsrc_t hrs =
         __builtin_amdgcn_make_buffer_rsrc(ghist, (short)0, fits ? (uint32_t)nchunk * kBins * 2u : 0u, 0x00020000);
     const uint32_t mt = ws_buffer_load32(mrs, (uint32_t)tid * 4u);
-  #pragma unroll
+#pragma unroll
     for (int p = 0; p < PA; ++p) v[p] = ws_buffer_load64(grs, (uint32_t)(p * NT + tid) * 8u);
     // The union's histogram: the sum of the chunks' published histograms
     // (one packed load per chunk per lane), 32 chunks' loads in flight at a
     // time (one round trip up to 32 chunks).
     for (int c0 = 0; c0 < (fits ? nchunk : 0); c0 += 32) {
       uint32_t h[32];
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < 32; ++u)
         h[u] = ws_buffer_load32(hrs, ((uint32_t)(c0 + u) * (kBins / 2) + (uint32_t)(kBins / 2 - 1 - tid)) * 4u);
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < 32; ++u) {
         hs[0] += h[u] >> 16;
         hs[1] += h[u] & 0xFFFFu;
       }
     }
-  #pragma unroll
+#pragma unroll
     for (int p = 0; p < PA; ++p) v[p] = p * NT + tid < nall ? v[p] : kNoCand;
     pf.issue();
     if (tid < nchunk) atomicMax(&s.bmax, mt & 0xFFFFu);
-    if (tid == 0) s.emit = 0;
+    // The boundary refinement's state, set up ahead of its barrier-free
+    // start: digit buffers 0 and 1, the AND / OR of the boundary keys
+    // (accumulated by the emission below) and the output counter.
+    for (int i = tid; i < 512; i += NT) s.hist[i] = 0;
+    if (tid == 0) {
+      s.emit = 0;
+      s.red_and[0] = ~0ull;
+      s.red_or[0] = 0ull;
+      s.out_ctr = 0;
+    }
     pf.commit(s);
     __syncthreads();
     uint32_t T = 0, above = 0, inT = 0;
@@ -1229,7 +1252,7 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
     if (fast) {
       // Code per slot: bin + 1 for a candidate, 0 for an unused slot.
       uint32_t code[PA];
-  #pragma unroll
+#pragma unroll
       for (int p = 0; p < PA; ++p) {
         const uint32_t b = bin_of(__uint_as_float((uint32_t)(v[p] >> 32))) + 1u;
         code[p] = v[p] != kNoCand ? b : 0u;
@@ -1240,7 +1263,7 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
       // this lane's own scratch entries (no branch per slot).
       const uint32_t t1 = T + 1u;
       uint32_t upm = 0, eqm = 0;
-  #pragma unroll
+#pragma unroll
       for (int p = 0; p < PA; ++p) {
         upm |= (code[p] > t1 ? 1u : 0u) << p;
         eqm |= (code[p] == t1 ? 1u : 0u) << p;
@@ -1248,15 +1271,28 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
       const uint32_t base =
           wave_reserve_n(&s.emit, ((uint32_t)__builtin_popcount(upm) << 16) | (uint32_t)__builtin_popcount(eqm));
       uint32_t pu = base >> 16, pe = base & 0xFFFFu;
-  #pragma unroll
+      // AND / OR of the boundary keys' upper halves (the FP32 keys); when
+      // those are all equal the index halves are taken as all-different,
+      // which only adds radix passes over the index bits (exact either way).
+      uint32_t ka = ~0u, ko = 0u;
+#pragma unroll
       for (int p = 0; p < PA; ++p) {
         const uint32_t up = (upm >> p) & 1u, eq = (eqm >> p) & 1u;
         int32_t* du = up && pu < (uint32_t)k ? &s.chosen[pu] : &cs.trash32[tid];
         uint64_t* de = eq && pe < (uint32_t)kCkCand ? &s.cand[pe] : &cs.trash64[tid];
+        const uint64_t ck = composite_key(__uint_as_float((uint32_t)(v[p] >> 32)), (int)(uint32_t)v[p]);
         *du = (int)(uint32_t)v[p];
-        *de = composite_key(__uint_as_float((uint32_t)(v[p] >> 32)), (int)(uint32_t)v[p]);
+        *de = ck;
+        ka &= eq ? (uint32_t)(ck >> 32) : ~0u;
+        ko |= eq ? (uint32_t)(ck >> 32) : 0u;
         pu += up;
         pe += eq;
+      }
+      ka = wave_bits32<true>(ka);
+      ko = wave_bits32<false>(ko);
+      if (lane_id() == 0) {
+        atomicAnd(&s.red_and[0], (uint64_t)ka << 32);
+        atomicOr(&s.red_or[0], ((uint64_t)ko << 32) | 0xFFFFFFFFull);
       }
       __syncthreads();
       const uint32_t nc = s.emit & 0xFFFFu, need = (uint32_t)k - above;
@@ -1267,7 +1303,7 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
           } else if (nc <= (uint32_t)kRankMax) {
             rank_refine<NT>(s, nc, need, nullptr, s.chosen, above);
           } else {
-            block_refine<NT>(s, nc, need, nullptr, s.chosen, above, k);
+            block_refine<NT, kCkCand, kCkPages, true>(s, nc, need, nullptr, s.chosen, above, k);
           }
           __syncthreads();
         } else {
