@@ -68,6 +68,8 @@ constexpr int kManyNT = 256;                   // row kernel for many rows: lane
 constexpr int kManyVpt = 64;                   // ...values per lane in registers
 constexpr int kManyCand = 1024;                // ...boundary candidates in LDS
 constexpr int kManyMinRows = 1024;             // batches with at least this many rows
+constexpr int kSmallNT = 512;                  // row kernel for short rows in small batches: lanes per workgroup
+constexpr int kSmallVpt = 4;                   // ...values per lane (rows of up to 2,048 entries)
 constexpr int kLongMin = 32769;                // rows this long are split over several workgroups
 constexpr int kCkNT = 512;                     // long rows: lanes per workgroup (1,024 measured slower)
 constexpr int kCkVpt = 16;                     // ...values per lane
@@ -751,7 +753,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP, RP>& s, const float* 
           if (keep) s.chosen[at] = idx;
         }
       }
-    } else if (NT != kManyNT && nc <= (uint32_t)kRankMax && nc <= (uint32_t)NT) {
+    } else if (!(NT == kManyNT && V == kManyVpt) && nc <= (uint32_t)kRankMax && nc <= (uint32_t)NT) {
       rank_refine<NT, CAP>(s, nc, need, out, chosen, above);
     } else {
       block_refine<NT, CAP>(s, nc, need, out, chosen, above, m);
@@ -955,12 +957,18 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP, RP>& s, const f
   if (TRANSLATE) translate_row<NT>(tr, pf.g, r, m, s.chosen, s.row_pages, (int)s.row_npages);
 }
 
-// One workgroup of NT lanes per row.  Three shapes: 1,024 lanes holding 16
+// One workgroup of NT lanes per row.  Four shapes: 1,024 lanes holding 16
 // entries each when the batch has few rows (each row gets a whole CU; longer
 // rows are streamed), 512 lanes holding 64 entries each for rows of up to
 // 32,768 entries (two rows per CU, one pass), 256 lanes holding 64 entries
 // each when it has many rows (several rows per CU, so one row's latency chain
-// overlaps the others').
+// overlaps the others'), and 512 lanes holding 4 entries each for rows of up
+// to 2,048 entries in small batches.  A single 2,048-entry row measured
+// 8.5 us (1,024 x 16), 7.4 us (128 x 16), 6.8 us (1,024 x 2), 6.4 us
+// (256 x 8) and 5.8 us (512 x 4) in the kernel trace: this selection is one
+// workgroup's latency chain, and both its barriers (more waves) and its
+// unrolled per-entry code (more entries per lane, cold in the instruction
+// cache on the compute unit that runs it) lengthen it.
 template <bool TRANSLATE, int NT, int VPT, int CAP>
 __global__ __launch_bounds__(NT, NT == kManyNT ? 4 : NT == kMidNT ? 2 : 1) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
@@ -1582,6 +1590,9 @@ static int launch_select(const float* scores, int64_t ld, const int32_t* row_len
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   } else if (max_len > kRowNT * kRowVpt) {
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kMidNT, kMidVpt, kMidCand>), dim3(num_rows), dim3(kMidNT), 0,
+                       stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
+  } else if (max_len <= kSmallNT * kSmallVpt) {
+    hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kSmallNT, kSmallVpt, kRowCand>), dim3(num_rows), dim3(kSmallNT), 0,
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   } else {
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kRowNT, kRowVpt, kRowCand>), dim3(num_rows), dim3(kRowNT), 0,
