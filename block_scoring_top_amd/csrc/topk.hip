@@ -1503,8 +1503,20 @@ __global__ __launch_bounds__(NT, 1) void topk_planned_kernel(
   const int r = cur.x, n = max(0, min(cur.z, max_len));
   if ((unsigned)r >= (unsigned)num_rows) return;  // never, for a plan made for this batch
   if (cur.y == kPlanWhole) {
-    select_whole_row<NT, kCkVpt, kCkCand, TRANSLATE>(cs.t, scores + (int64_t)r * ld, n, min(k, n), k,
-                                                     sel + (int64_t)r * k, sel_count, r, tr);
+    // The row in registers, in the shape that holds it with the fewest
+    // entries per lane (the short-row shapes' latency grows with the entries
+    // per lane); streamed only for lengths no plan of this batch gives a
+    // whole-row item.
+    const float* row = scores + (int64_t)r * ld;
+    int32_t* out = sel + (int64_t)r * k;
+    if (n <= NT * kSmallVpt)
+      select_whole_row<NT, kSmallVpt, kCkCand, TRANSLATE, false>(cs.t, row, n, min(k, n), k, out, sel_count, r, tr);
+    else if (n <= NT * kCkVpt)
+      select_whole_row<NT, kCkVpt, kCkCand, TRANSLATE, false>(cs.t, row, n, min(k, n), k, out, sel_count, r, tr);
+    else if (n <= NT * kMidVpt)
+      select_whole_row<NT, kMidVpt, kCkCand, TRANSLATE, false>(cs.t, row, n, min(k, n), k, out, sel_count, r, tr);
+    else
+      select_whole_row<NT, kCkVpt, kCkCand, TRANSLATE, true>(cs.t, row, n, min(k, n), k, out, sel_count, r, tr);
   } else if (n >= cut && (unsigned)cur.y < (unsigned)min(wmax, (n + kCkChunk - 1) / kCkChunk)) {
     chunk_item<TRANSLATE, NT, true>(cs, r, cur.y, n, cut, scores, ld, nullptr, max_len, k, sel, sel_count, ws,
                                     rec_bytes, wmax, tr);
