@@ -229,6 +229,28 @@ def test_topk_long_rows_many(R):
         check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_topk_very_long_rows(fused):
+    # Rows far past the headline length: at 200,000 entries and k = 2,048 the
+    # resolving workgroup holds 16 candidate slots per lane (4,800 slots); at
+    # 1,000,000 entries the candidate slots (11,808) exceed what it holds and
+    # it selects the whole row by streaming it; a short row rides along.
+    rng = np.random.default_rng(2100)
+    n = 1_000_000
+    rows = rng.standard_normal((3, n)).astype(np.float32)
+    rows[1, 500_000:510_000] += np.float32(3.0)  # winners clustered in one chunk
+    lens = np.array([200_000, n, 5000], dtype=np.int32)
+    for k in (2048, 512):
+        if fused:
+            c = 1
+            inp = _given_rows_batch(rng, [int(x) + 1 for x in lens], c, k)
+            _check_given(inp, rows, lens, _select_translate_given(inp, rows, lens, n))
+        else:
+            (out,), _ = gu.gpu_topk(rows, lens, k)
+            ref_sel, ref_cnt = oracle.topk(rows, lens, k)
+            check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
+
+
 def test_topk_overflowing_boundary_bin():
     # more than 4,096 entries tie in the boundary bin: exercises the re-scan refinement
     rng = np.random.default_rng(8)
