@@ -1076,7 +1076,7 @@ __device__ __forceinline__ uint64_t ws_load64(const uint64_t* p) {
 // by its w == 0 item (its other items do nothing); with KNOWN_N the caller
 // gives the length and passes only chunks of rows split at `cut`.  All lanes
 // call; every return is uniform.
-template <bool TRANSLATE, int NT, bool KNOWN_N>
+template <bool TRANSLATE, int NT, bool KNOWN_N, int ALL = kCkAll>
 __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_given, int cut,
                                            const float* __restrict__ scores, int64_t ld,
                                            const int32_t* __restrict__ row_len, int32_t max_len, int32_t k,
@@ -1200,11 +1200,14 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
 
   // ---- Resolution (the last chunk to arrive) ----
   const int nall = nchunk * Q;
-  const bool fits = nall <= kCkAll && nchunk <= kCkMeta;
+  const bool fits = nall <= ALL && nchunk <= kCkMeta;
   // The candidates are held PA per lane: 8 when they fit (most rows), else
-  // 16.  Two copies of the resolution, so that the common one carries half
-  // the registers and instructions (its code is cold on the compute unit
-  // that resolves, so its length costs time too).
+  // 16, else (ALL = 16,384: the one-launch grid, whose few workgroups per row
+  // leave room for the registers) 32, which keeps rows of about a million
+  // entries at k = 2,048 off the streaming fallback.  Separate copies of the
+  // resolution, so that the common one carries the fewest registers and
+  // instructions (its code is cold on the compute unit that resolves, so its
+  // length costs time too).
   auto resolve = [&](auto pa_tag) __attribute__((always_inline)) {
     constexpr int PA = decltype(pa_tag)::value;
     RowPagePrefetch<NT, TRANSLATE, kCkPages> pf{tr, r, gr};
@@ -1329,10 +1332,13 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
       select_whole_row<NT, VPT, kCkCand, TRANSLATE>(s, row, n, k, k, out, sel_count, r, tr);
     }
   };
-  if (nall <= 8 * NT)
+  if (nall <= 8 * NT) {
     resolve(IntTag<8>{});
-  else
+  } else if (ALL <= kCkAll || nall <= kCkAll) {
     resolve(IntTag<kCkAll / NT>{});
+  } else {
+    if constexpr (ALL > kCkAll) resolve(IntTag<ALL / NT>{});
+  }
   // Leave the first word of every kWsBlock-byte block of the row's record
   // zero: every layout a later call may lay over the workspace (other row
   // counts, lengths, k) puts its row counters on such words, and everything
@@ -1349,7 +1355,7 @@ __global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
     int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
     int64_t rec_bytes, int32_t wmax, Translate tr) {
   __shared__ ChunkShared cs;
-  chunk_item<TRANSLATE, NT, false>(cs, blockIdx.x, blockIdx.y, 0, kLongMin, scores, ld, row_len, max_len, k, sel,
+  chunk_item<TRANSLATE, NT, false, 2 * kCkAll>(cs, blockIdx.x, blockIdx.y, 0, kLongMin, scores, ld, row_len, max_len, k, sel,
                                    sel_count, ws, rec_bytes, wmax, tr);
 }
 

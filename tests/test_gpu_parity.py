@@ -231,19 +231,21 @@ def test_topk_long_rows_many(R):
 
 @pytest.mark.parametrize("fused", [False, True])
 def test_topk_very_long_rows(fused):
-    # Rows far past the headline length: at 200,000 entries and k = 2,048 the
-    # resolving workgroup holds 16 candidate slots per lane (4,800 slots); at
-    # 1,000,000 entries the candidate slots (11,808) exceed what it holds and
-    # it selects the whole row by streaming it; a short row rides along.
+    # Rows far past the headline length, through every form of the long-row
+    # resolution: at 200,000 entries and k = 2,048 the resolving workgroup
+    # holds 16 candidate slots per lane (4,800 slots), at 1,000,000 entries 32
+    # (11,808 slots); a 1,000,000-entry row whose winners cluster in one chunk
+    # fails the exactness check and is selected whole by streaming, and so is
+    # a 2,000,000-entry row, whose candidate slots (23,520) exceed what the
+    # resolving workgroup holds; a short row rides along.
     rng = np.random.default_rng(2100)
-    n = 1_000_000
-    rows = rng.standard_normal((3, n)).astype(np.float32)
-    rows[1, 500_000:510_000] += np.float32(3.0)  # winners clustered in one chunk
-    lens = np.array([200_000, n, 5000], dtype=np.int32)
+    n = 2_000_000
+    lens = np.array([200_000, 1_000_000, 1_000_000, n, 5000], dtype=np.int32)
+    rows = rng.standard_normal((lens.size, n)).astype(np.float32)
+    rows[2, 500_000:510_000] += np.float32(3.0)  # winners clustered in one chunk
     for k in (2048, 512):
         if fused:
-            c = 1
-            inp = _given_rows_batch(rng, [int(x) + 1 for x in lens], c, k)
+            inp = _given_rows_batch(rng, [int(x) + 1 for x in lens], 1, k)
             _check_given(inp, rows, lens, _select_translate_given(inp, rows, lens, n))
         else:
             (out,), _ = gu.gpu_topk(rows, lens, k)
