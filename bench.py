@@ -174,14 +174,20 @@ def time_steps(fns, K, warmup, stream, probe=0, probe_every=10, burst=20):
 
 def cold_steps(fns, reps, stream, flush_bytes=512 << 20):
     """Median step time with the 256 MB Infinity Cache flushed before every
-    step: a `flush_bytes` scratch buffer is written between steps, outside
-    the events that bracket each step."""
+    step: a `flush_bytes` scratch buffer is read (a reduction over it) between
+    steps, outside the events that bracket each step.  Reading, not writing:
+    a written buffer leaves the cache full of dirty lines, whose write-back
+    would then run inside the timed step.  The scratch is written once and
+    read twice before the first step, so the lines it leaves are clean."""
     import numpy as np
     import torch
-    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device=torch.cuda.current_device())
+    scratch = torch.zeros(flush_bytes // 8, dtype=torch.int64, device=torch.cuda.current_device())
+    for _ in range(2):
+        scratch.sum()
+    torch.cuda.synchronize()
     times = []
     for i in range(reps):
-        scratch.fill_(i & 0xFF)
+        scratch.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for f in fns:
@@ -338,8 +344,8 @@ def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
            "roofline": roof, "step_roofline": step_roof}
     if cold:
         out["cold_ms_per_step"] = round(cold, 5)
-        out["cold_note"] = ("median of 20 steps, each after writing a 512 MiB scratch buffer (flushes the 256 MB "
-                            "Infinity Cache), outside the events")
+        out["cold_note"] = ("median of 20 steps, each after a reduction over a 512 MiB scratch buffer (reads "
+                            "evict the 256 MB Infinity Cache and leave it clean), outside the events")
     return out
 
 
