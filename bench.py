@@ -119,6 +119,14 @@ def cpu_baseline(inp, min_seconds: float):
                       f"{el:.1f} s"}
 
 
+def bound(fns, stream):
+    """Prepared calls with the stream fixed once (each call is then a single C
+    call: looking up torch's current stream costs ~2.7 us of host time per
+    call, which made the small steps host-bound)."""
+    import block_scoring_top_amd as bst
+    return [f.bind(stream) if isinstance(f, bst.PreparedCall) else f for f in fns]
+
+
 def time_steps(fns, K, warmup, stream, probe=0, probe_every=10, burst=20):
     """Runs the callables of a step K times after `warmup` untimed steps and
     returns (ms per step, dict of dominant-kernel timings).
@@ -136,6 +144,7 @@ def time_steps(fns, K, warmup, stream, probe=0, probe_every=10, burst=20):
         a kernel queued behind an event marker, a few microseconds)."""
     import numpy as np
     import torch
+    fns = bound(fns, stream)
     for _ in range(warmup):
         for f in fns:
             f()
@@ -181,6 +190,7 @@ def cold_steps(fns, reps, stream, flush_bytes=512 << 20):
     read twice before the first step, so the lines it leaves are clean."""
     import numpy as np
     import torch
+    fns = bound(fns, stream)
     scratch = torch.zeros(flush_bytes // 8, dtype=torch.int64, device=torch.cuda.current_device())
     for _ in range(2):
         scratch.sum()
@@ -240,6 +250,7 @@ def kernel_breakdown(fns, K, stream):
     separate pass after the timed region (for the per-kernel report only)."""
     import numpy as np
     import torch
+    fns = bound(fns, stream)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):

@@ -388,6 +388,30 @@ class PreparedCall:
         if st != 0:
             _check(st, self.fn)
 
+    def bind(self, stream=None) -> "BoundCall":
+        """The same call with the stream resolved now (default: the current
+        stream): each call is then one C call with nothing looked up."""
+        return BoundCall(self, _stream(stream, self.device))
+
+
+class BoundCall:
+    """A PreparedCall with its stream fixed; ``__call__`` takes no arguments."""
+
+    __slots__ = ("fn", "_f", "_args")
+
+    def __init__(self, prepared: PreparedCall, stream_ptr):
+        self.fn = prepared.fn
+        self._f = prepared._f
+        # Arguments as instances of their declared C types, so that a call
+        # converts nothing.
+        args = (*prepared.args, stream_ptr)
+        self._args = tuple(a if isinstance(a, t) else t(a) for a, t in zip(args, self._f.argtypes))
+
+    def __call__(self):
+        st = self._f(*self._args)
+        if st != 0:
+            _check(st, self.fn)
+
 
 def prepare_score(fn: str, q, kcache, num_pages, page_table, req_row_ptr, row_pos, c, max_vis, scores,
                   row_len=None) -> PreparedCall:
@@ -439,7 +463,7 @@ __all__ = [
     "idx_score_decode", "idx_score_prefill", "topk_workspace_bytes", "topk_workspace",
     "topk_select_rows", "idx_expand_translate", "idx_expand_translate_shared", "idx_select_translate",
     "idx_select_translate_noalloc", "NOALLOC_SCRATCH_BYTES", "idx_compress_store", "status_string", "BlockScoreError",
-    "lib", "PreparedCall", "prepare_score", "prepare_topk", "prepare_select_translate", "prepare_expand_shared",
+    "lib", "PreparedCall", "BoundCall", "prepare_score", "prepare_topk", "prepare_select_translate", "prepare_expand_shared",
     "prepare_compress_store", "topk_plan_bytes", "topk_planned_workspace_bytes", "topk_plan",
     "topk_planned_workspace", "topk_plan_rows", "idx_select_translate_planned", "prepare_plan",
     "prepare_select_translate_planned",

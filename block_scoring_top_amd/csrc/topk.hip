@@ -1365,14 +1365,14 @@ __device__ __forceinline__ void chunk_item(ChunkShared& cs, int r, int w, int n_
 
 // One workgroup per (row, chunk) of the grid; rows shorter than kLongMin are
 // selected whole by their first workgroup.
-template <bool TRANSLATE, int NT>
+template <bool TRANSLATE, int NT, int ALL>
 __global__ __launch_bounds__(NT, 1) void topk_chunked_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
     int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws,
     int64_t rec_bytes, int32_t wmax, Translate tr) {
   __shared__ ChunkShared cs;
-  chunk_item<TRANSLATE, NT, false, 2 * kCkAll>(cs, blockIdx.x, blockIdx.y, 0, kLongMin, scores, ld, row_len, max_len, k, sel,
-                                   sel_count, ws, rec_bytes, wmax, tr);
+  chunk_item<TRANSLATE, NT, false, ALL>(cs, blockIdx.x, blockIdx.y, 0, kLongMin, scores, ld, row_len, max_len, k, sel,
+                                        sel_count, ws, rec_bytes, wmax, tr);
 }
 
 // Planning (TopK-V2: a planning kernel reads the batch's row lengths once,
@@ -1616,9 +1616,20 @@ static int launch_select(const float* scores, int64_t ld, const int32_t* row_len
                          hipStream_t stream) {
   if (use_long_path(max_len)) {
     const int wmax = (max_len + kCkChunk - 1) / kCkChunk;
-    hipLaunchKernelGGL((topk_chunked_kernel<TRANSLATE, kCkNT>), dim3(num_rows, wmax), dim3(kCkNT), 0, stream, scores, ld,
-                       row_len, max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace),
-                       (int64_t)ck_record_bytes(max_len, k), wmax, tr);
+    // The resolver that holds 32 candidates per lane needs twice the
+    // registers (one workgroup per CU instead of two): launched only when a
+    // row of max_len entries has more candidate slots than the 16-per-lane
+    // form holds (about a million entries at k = 2,048).  Either form is exact
+    // for every row; a row beyond its capacity is streamed whole.
+    const int64_t slots = (int64_t)wmax * ck_slots<kCkChunk>(std::max(max_len, kLongMin), k);
+    if (slots > kCkAll)
+      hipLaunchKernelGGL((topk_chunked_kernel<TRANSLATE, kCkNT, 2 * kCkAll>), dim3(num_rows, wmax), dim3(kCkNT), 0,
+                         stream, scores, ld, row_len, max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace),
+                         (int64_t)ck_record_bytes(max_len, k), wmax, tr);
+    else
+      hipLaunchKernelGGL((topk_chunked_kernel<TRANSLATE, kCkNT, kCkAll>), dim3(num_rows, wmax), dim3(kCkNT), 0,
+                         stream, scores, ld, row_len, max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace),
+                         (int64_t)ck_record_bytes(max_len, k), wmax, tr);
   } else if (num_rows >= kManyMinRows && max_len <= kManyNT * kManyVpt) {
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kManyNT, kManyVpt, kManyCand>), dim3(num_rows), dim3(kManyNT), 0,
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
