@@ -97,6 +97,12 @@ class IndexerPath:
                                      self.sel, self.sel_count, self.slots, self.out_count, self.plan_buf,
                                      out_pos=self.pos, workspace=self.planned_workspace, stream=stream)
 
+    def bound(self, stream=None):
+        """(score, select_translate) with arguments and stream fixed: each is
+        one C call taking no arguments (for loops that run the step many
+        times on one stream)."""
+        return tuple(c.bind(stream) for c in self.prepared())
+
     def prepared(self):
         """(score, select_translate) as prepared calls: each takes an optional
         stream and launches with no per-call argument checking."""

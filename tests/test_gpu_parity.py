@@ -139,6 +139,34 @@ def test_decode_planned_end_to_end(wl):
     _full_check(inp, planned=True)
 
 
+def test_bound_calls_match_prepared():
+    # The step through calls bound to a stream gives the same outputs as the
+    # prepared calls on the current stream (and as the oracle).
+    from block_scoring_top_amd.pipeline import IndexerPath
+    from synth.device import upload
+    inp = synth.qsa_verify_64req(B=4, lo=300, hi=9000)
+    gu.say("bound calls vs prepared calls")
+    p = IndexerPath(upload(inp, "cuda"), "decode")
+    p.run()
+    torch.cuda.synchronize()
+    want = [t.cpu().numpy().copy() for t in (p.scores, p.row_len, p.sel_count, p.out_count)]
+    sel_w = np.sort(p.sel.cpu().numpy(), 1)
+    for t in (p.scores, p.sel, p.sel_count, p.slots, p.out_count):
+        t.fill_(-3)
+    stream = torch.cuda.Stream()
+    score, select = p.bound(stream)
+    score()
+    select()
+    stream.synchronize()
+    got = [t.cpu().numpy() for t in (p.scores, p.row_len, p.sel_count, p.out_count)]
+    rl = want[1]
+    for r in range(inp.num_rows):
+        assert np.array_equal(got[0][r, :rl[r]].view(np.uint32), want[0][r, :rl[r]].view(np.uint32))
+    for a, b in zip(got[1:], want[1:]):
+        assert np.array_equal(a, b)
+    assert np.array_equal(np.sort(p.sel.cpu().numpy(), 1), sel_w)
+
+
 def test_decode_leaves_invisible_entries_untouched():
     inp = synth.qsa_verify_64req(B=5, lo=500, hi=6000)
     s, rl = gu.gpu_scores(inp, ld=inp.max_vis + 40)
