@@ -1509,7 +1509,7 @@ __global__ __launch_bounds__(kPlanNT) void topk_plan_kernel(const int32_t* __res
 // keeps its per-lane invariants live across iterations and needs 195 VGPRs
 // (one workgroup per compute unit) where one item per workgroup needs 111
 // (two).
-template <bool TRANSLATE, int NT>
+template <bool TRANSLATE, int NT, int ALL = kCkAll>
 __global__ __launch_bounds__(NT, 1) void topk_planned_kernel(
     const float* __restrict__ scores, int64_t ld, int32_t num_rows, int32_t max_len, int32_t k,
     int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, uint8_t* __restrict__ ws, int64_t rec_bytes,
@@ -1540,8 +1540,8 @@ __global__ __launch_bounds__(NT, 1) void topk_planned_kernel(
     else
       select_whole_row<NT, kCkVpt, kCkCand, TRANSLATE, true>(cs.t, row, n, min(k, n), k, out, sel_count, r, tr);
   } else if (n >= cut && (unsigned)cur.y < (unsigned)min(wmax, (n + kCkChunk - 1) / kCkChunk)) {
-    chunk_item<TRANSLATE, NT, true>(cs, r, cur.y, n, cut, scores, ld, nullptr, max_len, k, sel, sel_count, ws,
-                                    rec_bytes, wmax, tr);
+    chunk_item<TRANSLATE, NT, true, ALL>(cs, r, cur.y, n, cut, scores, ld, nullptr, max_len, k, sel, sel_count, ws,
+                                         rec_bytes, wmax, tr);
   }
 }
 
@@ -1601,8 +1601,15 @@ int launch_select_translate_planned(const float* scores, int64_t ld, int32_t num
   const int grid = (int)topk_plan_items(num_rows, max_len);
   const int wmax = std::max(1, (max_len + kCkChunk - 1) / kCkChunk);
   const int64_t rec = max_len >= kPlanMinCut ? (int64_t)ck_record_bytes(max_len, k, kPlanMinCut) : 0;
-  hipLaunchKernelGGL((topk_planned_kernel<true, kCkNT>), dim3(grid), dim3(kCkNT), 0, stream, scores, ld, num_rows,
-                     max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace), rec, wmax, plan, tr);
+  // As in the one-launch grid: the 32-per-lane resolver only when a max_len
+  // row has more candidate slots than the 16-per-lane form holds.
+  const int64_t slots = (int64_t)wmax * ck_slots<kCkChunk>(std::max(max_len, kPlanMinCut), k);
+  if (slots > kCkAll)
+    hipLaunchKernelGGL((topk_planned_kernel<true, kCkNT, 2 * kCkAll>), dim3(grid), dim3(kCkNT), 0, stream, scores, ld,
+                       num_rows, max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace), rec, wmax, plan, tr);
+  else
+    hipLaunchKernelGGL((topk_planned_kernel<true, kCkNT>), dim3(grid), dim3(kCkNT), 0, stream, scores, ld, num_rows,
+                       max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace), rec, wmax, plan, tr);
   return hipGetLastError() == hipSuccess ? BS_OK : BS_ERR_LAUNCH;
 }
 

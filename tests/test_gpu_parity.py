@@ -851,6 +851,21 @@ def test_planned_rows_past_the_register_blocks():
     assert _check_planned(rows, lens, 40000, header, outs) == 32769
 
 
+def test_planned_very_long_rows():
+    # The planned launch on rows whose candidate slots need the resolver's
+    # larger forms: 1,000,000 entries (11,808 slots at k = 2,048: 32 per
+    # lane), 200,000 (16 per lane) and 16,385 (split into 3 chunks, 16 per
+    # lane), with a whole-row item beside them.
+    rng = np.random.default_rng(2200)
+    n = 1_000_000
+    lens = np.array([n, 200_000, 16_385, 5000], dtype=np.int32)
+    rows = rng.standard_normal((lens.size, n)).astype(np.float32)
+    ctx = [int(x) + 1 for x in lens]
+    inp = _given_rows_batch(rng, ctx, 1, 2048)
+    header, outs = _planned_given(inp, rows, lens, n, ks=[2048, 512], reps=1)
+    assert _check_planned(rows, lens, n, header, outs) == 16385
+
+
 def test_planned_short_rows_only():
     # max_len below 16,385: no workspace, one whole-row item per row, every
     # length edge (0, 1, k - 1, k, k + 1, a full register tile, past it).
