@@ -73,16 +73,17 @@ def source_digest(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, digest: str):
+def measured_traffic(kernel: str, digest: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+    it was taken on the current kernel source and on this workload; else
+    None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_digest") != digest:
+    if rec.get("source_digest") != digest or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -316,13 +317,17 @@ def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
     method = (f"HIP events on the launch stream around {kt['burst']} back-to-back launches, right after the "
               "timed region")
     if scorer == "decode":
-        kname, dig = "score_decode_kernel", source_digest("score_decode.hip", "device.h")
+        # More than two rows per request (rounded up) go to the matrix-core
+        # rows kernel; the traffic record holds the VALU kernel only.
+        mfma_rows = -(-inp.num_rows // inp.num_req) > 2
+        kname = "score_rows_mfma_kernel" if mfma_rows else "score_decode_kernel"
+        dig = source_digest("score_decode.hip", "device.h")
         alg = scorer_bytes(inp)
         ach = alg / (t_score * 1e-3) / 1e9
         tr = kernel_trace_us(f"{name}:{kname}", dig)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("score_decode", dig),
+                "traffic": None if mfma_rows else measured_traffic("score_decode", dig, name),
                 "kernel": kname, "algorithmic_bytes": alg, "avg_us": round(t_score * 1e3, 2), "avg_us_method": method,
                 "avg_us_in_steps": round(kt["in_steps_ms"] * 1e3, 2),
                 "kernel_trace_avg_us": tr,
@@ -334,7 +339,7 @@ def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
         tr = kernel_trace_us(f"{name}:{kname}", dig)
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("score_prefill", dig),
+                "traffic": measured_traffic("score_prefill", dig, name),
                 "kernel": kname, "algorithmic_flops": fl, "avg_us": round(t_score * 1e3, 2), "avg_us_method": method,
                 "avg_us_in_steps": round(kt["in_steps_ms"] * 1e3, 2),
                 "kernel_trace_avg_us": tr,
