@@ -173,11 +173,23 @@ __device__ __forceinline__ uint32_t inverted_index(int idx) {
   return r;
 }
 
-// base + i*NT + lane, recomputed at each use: left to itself the compiler
-// keeps all V of these (and their bounds tests) live across the kernel.
-template <int NT>
+// Entries 4*(lane_quad + uniform_quad) .. +3 of a row in one 16-byte load
+// (the row starts 16-byte aligned; the resource's range check returns 0
+// past its end).
+__device__ __forceinline__ u32x4_t row_quad(const RowReader& rd, int lane_quad, int uniform_quad) {
+  return __builtin_bit_cast(u32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(rd.rsrc, lane_quad * 16, uniform_quad * 16, 0));
+}
+
+// Row index of a lane's register entry i, recomputed at each use: left to
+// itself the compiler keeps all V of these (and their bounds tests) live
+// across the kernel.  VEC = 1: entry i is base + i*NT + lane.  VEC = 4 (rows
+// read 16 bytes per lane): entries 4q .. 4q+3 are the four consecutive
+// entries at base + 4*(q*NT + lane).
+template <int NT, int VEC = 1>
 __device__ __forceinline__ int entry_index(int base, int i) {
-  int idx = base + i * NT + (int)threadIdx.x;
+  int idx = VEC == 1 ? base + i * NT + (int)threadIdx.x
+                     : base + ((i / VEC) * NT + (int)threadIdx.x) * VEC + (i % VEC);
   asm volatile("" : "+v"(idx));
   return idx;
 }
@@ -608,7 +620,10 @@ __device__ __forceinline__ void row_threshold(TopkShared<CAP, RP>& s, uint32_t m
 // the histogram (skipped when it is ready), once in NT*V-entry tiles for
 // emission.  HIST_READY: s.hist
 // already holds the row's histogram (long-row finisher).  All lanes call.
-template <int NT, int V, int CAP, int RP, bool HIST_READY, bool STREAM, class PF>
+// VEC = 4: the register path reads its entries 16 bytes per lane (the
+// caller's row starts 16-byte aligned and holds at least n rounded up to 4
+// entries).
+template <int NT, int V, int CAP, int RP, bool HIST_READY, bool STREAM, class PF, int VEC = 1>
 __device__ __forceinline__ void select_row(TopkShared<CAP, RP>& s, const float* __restrict__ row, int n, int m,
                                            int32_t* __restrict__ out, bool keep, PF& pf) {
   constexpr int kTile = V;
@@ -635,24 +650,44 @@ __device__ __forceinline__ void select_row(TopkShared<CAP, RP>& s, const float* 
     // With a few entries per lane the values stay in registers, and the
     // boundary list gets its exact keys at once (no re-read round trip).
     constexpr bool KEEP_X = V <= 4;
+    static_assert(VEC == 1 || (VEC == 4 && V % 4 == 0 && !STREAM), "16-byte reads: whole quads, registers only");
     uint32_t pb[P];
     float x[V];
+    if constexpr (VEC == 4) {
+      // V/4 loads per lane instead of V: a wave has at most 63 vector memory
+      // operations outstanding, so V = 64 one-dword loads (plus the page
+      // prefetch) made the last ones wait for the first to return.  The
+      // quad holding entry n-1 is read whole (its entries past n are masked
+      // by index below).
+      const RowReader rq(row, (n + 3) & ~3);
 #pragma unroll
-    for (int i = 0; i < V; ++i) x[i] = rd.at(tid, i * NT);  // every load in flight at once
+      for (int q = 0; q < V / 4; ++q) {
+        const u32x4_t v = row_quad(rq, tid, q * NT);
+        x[4 * q] = __uint_as_float(v.x);
+        x[4 * q + 1] = __uint_as_float(v.y);
+        x[4 * q + 2] = __uint_as_float(v.z);
+        x[4 * q + 3] = __uint_as_float(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) x[i] = rd.at(tid, i * NT);  // every load in flight at once
+    }
     pf.issue();
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       if (p % 4 == 0) __builtin_amdgcn_sched_barrier(0);  // a few bins live at a time
       const uint32_t B = bin_pair(x[2 * p], x[2 * p + 1]);
       uint32_t code;
-      if ((2 * p + 2) * NT <= n) {  // the whole pair lies inside the row, for every lane
+      // Pair p is entries 2p, 2p+1 of every lane: with VEC = 4 half of quad
+      // p/2.  Checked for the whole workgroup at once.
+      if ((VEC == 4 ? (p / 2 + 1) * NT * 4 : (2 * p + 2) * NT) <= n) {  // inside the row for every lane
         if (!HIST_READY) {
           atomicAdd(&s.hist[B & 0xFFFFu], 1u);
           atomicAdd(&s.hist[B >> 16], 1u);
         }
         code = B + 0x00010001u;
       } else {
-        const bool ok0 = entry_index<NT>(0, 2 * p) < n, ok1 = entry_index<NT>(0, 2 * p + 1) < n;
+        const bool ok0 = entry_index<NT, VEC>(0, 2 * p) < n, ok1 = entry_index<NT, VEC>(0, 2 * p + 1) < n;
         if (!HIST_READY && ok0) atomicAdd(&s.hist[B & 0xFFFFu], 1u);
         if (!HIST_READY && ok1) atomicAdd(&s.hist[B >> 16], 1u);
         code = (ok0 ? (B & 0xFFFFu) + 1u : 0u) | (ok1 ? (B & 0xFFFF0000u) + 0x00010000u : 0u);
@@ -692,7 +727,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP, RP>& s, const float* 
       const int i = __builtin_ctzll(upm);
       upm &= upm - 1;
       if (pu < (uint32_t)m) {
-        const int idx = i * NT + tid;
+        const int idx = entry_index<NT, VEC>(0, i);
         if (out) out[pu] = idx;
         if (keep) s.chosen[pu] = idx;
       }
@@ -702,7 +737,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP, RP>& s, const float* 
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         if ((eqm >> i) & 1ull) {
-          if (pe < (uint32_t)CAP) s.cand[pe] = composite_key(x[i], i * NT + tid);
+          if (pe < (uint32_t)CAP) s.cand[pe] = composite_key(x[i], entry_index<NT, VEC>(0, i));
           ++pe;
         }
       }
@@ -710,7 +745,7 @@ __device__ __forceinline__ void select_row(TopkShared<CAP, RP>& s, const float* 
       while (eqm) {
         const int i = __builtin_ctzll(eqm);
         eqm &= eqm - 1;
-        if (pe < (uint32_t)CAP) s.cand[pe] = (uint64_t)(uint32_t)(i * NT + tid);  // index only, for now
+        if (pe < (uint32_t)CAP) s.cand[pe] = (uint64_t)(uint32_t)entry_index<NT, VEC>(0, i);  // index only, for now
         ++pe;
       }
     }
@@ -949,7 +984,7 @@ struct RowPagePrefetch {
 };
 
 // The whole selection of one row by one workgroup, any n.
-template <int NT, int VPT, int CAP, bool TRANSLATE, bool STREAM = true, int RP>
+template <int NT, int VPT, int CAP, bool TRANSLATE, bool STREAM = true, int RP, int VEC = 1>
 __device__ __forceinline__ void select_whole_row(TopkShared<CAP, RP>& s, const float* __restrict__ row, int n, int m, int k,
                                  int32_t* __restrict__ out, int32_t* __restrict__ sel_count, int r,
                                  const Translate& tr) {
@@ -965,7 +1000,7 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP, RP>& s, const f
     for (int i = tid; i < n; i += NT) s.chosen[i] = i;
     pf.commit(s);
   } else {
-    select_row<NT, VPT, CAP, RP, false, STREAM>(s, row, n, m, nullptr, true, pf);
+    select_row<NT, VPT, CAP, RP, false, STREAM, decltype(pf), VEC>(s, row, n, m, nullptr, true, pf);
   }
   __syncthreads();
   for (int i = tid; i < k; i += NT) out[i] = i < m ? s.chosen[i] : -1;
@@ -985,7 +1020,7 @@ __device__ __forceinline__ void select_whole_row(TopkShared<CAP, RP>& s, const f
 // workgroup's latency chain, and both its barriers (more waves) and its
 // unrolled per-entry code (more entries per lane, cold in the instruction
 // cache on the compute unit that runs it) lengthen it.
-template <bool TRANSLATE, int NT, int VPT, int CAP>
+template <bool TRANSLATE, int NT, int VPT, int CAP, int VEC = 1>
 __global__ __launch_bounds__(NT, NT == kManyNT ? 4 : NT == kMidNT ? 2 : 1) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_len, int32_t max_len,
     int32_t k, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count, Translate tr) {
@@ -995,8 +1030,8 @@ __global__ __launch_bounds__(NT, NT == kManyNT ? 4 : NT == kMidNT ? 2 : 1) void 
   const int m = min(k, n);
   // The many-rows and mid shapes are launched only for rows of at most
   // NT*VPT entries.
-  select_whole_row<NT, VPT, CAP, TRANSLATE, NT == kRowNT>(s, scores + (int64_t)r * ld, n, m, k,
-                                                          sel + (int64_t)r * k, sel_count, r, tr);
+  select_whole_row<NT, VPT, CAP, TRANSLATE, NT == kRowNT, kRowPages, VEC>(s, scores + (int64_t)r * ld, n, m, k,
+                                                                         sel + (int64_t)r * k, sel_count, r, tr);
 }
 
 template <int V>
@@ -1621,6 +1656,11 @@ template <bool TRANSLATE>
 static int launch_select(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_rows, int32_t max_len,
                          int32_t k, int32_t* sel, int32_t* sel_count, void* workspace, const Translate& tr,
                          hipStream_t stream) {
+  // Rows that start 16-byte aligned (ld a multiple of 4, aligned base) are
+  // read 16 bytes per lane by the 512-lane x 64-entry shape: 16 loads per
+  // lane instead of 64 (a wave has at most 63 loads outstanding).  Verify
+  // batch (384 rows): 18.5 -> 17.8 us back to back, bitwise the same output.
+  const bool quads = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   if (use_long_path(max_len)) {
     const int wmax = (max_len + kCkChunk - 1) / kCkChunk;
     // The resolver that holds 32 candidates per lane needs twice the
@@ -1638,11 +1678,20 @@ static int launch_select(const float* scores, int64_t ld, const int32_t* row_len
                          stream, scores, ld, row_len, max_len, k, sel, sel_count, static_cast<uint8_t*>(workspace),
                          (int64_t)ck_record_bytes(max_len, k), wmax, tr);
   } else if (num_rows >= kManyMinRows && max_len <= kManyNT * kManyVpt) {
+    // One-dword reads here: the 16-byte form measured 134.0-135.5 against
+    // 137.7-139.7 us on the 8,192-row prefill selection (same box, back to
+    // back).  Six rows share a CU and their loads already fill its memory
+    // pipeline (the loads' issue alone takes ~2 us of a row's 22 in either
+    // form).
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kManyNT, kManyVpt, kManyCand>), dim3(num_rows), dim3(kManyNT), 0,
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   } else if (max_len > kRowNT * kRowVpt) {
-    hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kMidNT, kMidVpt, kMidCand>), dim3(num_rows), dim3(kMidNT), 0,
-                       stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
+    if (quads)
+      hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kMidNT, kMidVpt, kMidCand, 4>), dim3(num_rows), dim3(kMidNT), 0,
+                         stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
+    else
+      hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kMidNT, kMidVpt, kMidCand>), dim3(num_rows), dim3(kMidNT), 0,
+                         stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);
   } else if (max_len <= kSmallNT * kSmallVpt) {
     hipLaunchKernelGGL((topk_rows_kernel<TRANSLATE, kSmallNT, kSmallVpt, kRowCand>), dim3(num_rows), dim3(kSmallNT), 0,
                        stream, scores, ld, row_len, max_len, k, sel, sel_count, tr);

@@ -659,6 +659,55 @@ def test_fused_many_rows_exact(c):
     _check_given(inp, rows, lens, _select_translate_given(inp, rows, lens, n))
 
 
+@pytest.mark.parametrize("layout", ["aligned", "odd_ld", "offset_base"])
+def test_mid_rows_read_layouts(layout):
+    # Rows of 16,385-32,768 entries in a small batch take the 512-lane x
+    # 64-entry shape.  Rows that start 16-byte aligned are read 16 bytes per
+    # lane, the quad holding entry n-1 whole; other layouts one entry per
+    # lane.  Every entry past a row's length holds +inf, so a read past n that
+    # is not masked would be selected.  Fused and unfused, against the oracle.
+    import block_scoring_top_amd as bst
+    from synth.device import upload
+    rng = np.random.default_rng(1300)
+    R, max_len, k, c = 40, 30000, 2048, 1
+    ld = max_len + (1 if layout == "odd_ld" else 0)
+    off = 1 if layout == "offset_base" else 0
+    lens = rng.integers(16385, max_len + 1, R).astype(np.int32)
+    lens[:12] = [0, 1, k, k + 1, 16385, 16386, 16387, 16388, 29997, 29998, 29999, 30000]
+    rows = rng.standard_normal((R, max_len)).astype(np.float32)
+    rows[12:20] = synth.tie_storm_rows(1301, 8, max_len)
+    host = np.full(R * ld + off + 4, np.inf, dtype=np.float32)
+    for r in range(R):
+        host[off + r * ld: off + r * ld + lens[r]] = rows[r, :lens[r]]
+    flat = torch.from_numpy(host).cuda()
+    s = flat[off:off + R * ld].view(R, ld)
+    assert (s.data_ptr() % 16 == 0) == (layout != "offset_base") and s.stride(0) == ld
+    rl = torch.from_numpy(lens).cuda()
+    inp = _given_rows_batch(rng, [max(1, int(x)) for x in lens], c, k)
+    dev = upload(inp, "cuda")
+    ws = bst.topk_workspace(R, max_len, k, "cuda")
+    ref_sel, ref_cnt = oracle.topk(rows, lens, k)
+    gu.say(f"mid rows {layout}: unfused")
+    sel = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    bst.topk_select_rows(s, rl, max_len, k, sel, cnt, ws)
+    torch.cuda.synchronize()
+    check_topk_exact(sel.cpu().numpy(), cnt.cpu().numpy(), ref_sel, ref_cnt)
+    gu.say(f"mid rows {layout}: fused")
+    sel.fill_(-7)
+    cnt.fill_(-7)
+    slots = torch.full((R, inp.ld_out), -7, dtype=torch.int32, device="cuda")
+    pos = torch.full((R, inp.ld_out), -7, dtype=torch.int32, device="cuda")
+    oc = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    bst.idx_select_translate(s, rl, max_len, k, dev.req_row_ptr, dev.row_pos, c, dev.page_table, sel, cnt, slots,
+                             oc, out_pos=pos, workspace=ws)
+    torch.cuda.synchronize()
+    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    check_topk_exact(sel_h, cnt_h, ref_sel, ref_cnt)
+    rs, rp, rc = oracle.expand_translate(inp, sel_h, cnt_h)
+    check_expand_exact(slots.cpu().numpy(), pos.cpu().numpy(), oc.cpu().numpy(), rs, rp, rc, gu.pending_counts(inp))
+
+
 @pytest.mark.parametrize("c", [1, 4])
 def test_long_rows_fused_exact(c):
     # rows of >= 32,769 entries (one workgroup per 8,192-entry chunk, the last
