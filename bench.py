@@ -360,6 +360,7 @@ def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
            "roofline": roof, "step_roofline": step_roof}
     if cold:
         out["cold_ms_per_step"] = round(cold, 5)
+        out["cold_rows_per_s"] = round(inp.num_rows / (cold * 1e-3), 1)
         out["cold_note"] = ("median of 20 steps, each after a reduction over a 512 MiB scratch buffer (reads "
                             "evict the 256 MB Infinity Cache and leave it clean), outside the events")
     return out
@@ -510,8 +511,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every other workload (extra field)")
     ap.add_argument("--unfused", action="store_true", help="separate top-k and expand calls")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time steps with the Infinity Cache flushed before each (always on with --all)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the steps timed with the Infinity Cache flushed before each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -538,14 +539,16 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
         return
-    res = run_workload(args.workload, args.steps, args.warmup, dev, fused=not args.unfused, cold_reps=args.cold)
+    res = run_workload(args.workload, args.steps, args.warmup, dev, fused=not args.unfused,
+                       cold_reps=not args.no_cold)
     inp = res.pop("_inp")
     extra = {}
     if args.all:
         for name in synth.WORKLOADS:
             if name == args.workload:
                 continue
-            r = run_workload(name, args.steps, args.warmup, dev, fused=not args.unfused, cold_reps=True)
+            r = run_workload(name, args.steps, args.warmup, dev, fused=not args.unfused,
+                             cold_reps=not args.no_cold)
             r.pop("_inp")
             extra[name] = r
     cpu = None
@@ -572,7 +575,7 @@ def main():
         "step_roofline": res.get("step_roofline"),
         "cpu_baseline": cpu,
     }
-    for key in ("cold_ms_per_step", "cold_note"):
+    for key in ("cold_ms_per_step", "cold_rows_per_s", "cold_note"):
         if key in res:
             line[key] = res[key]
     if extra:
