@@ -865,7 +865,11 @@ __device__ __forceinline__ RowGeom row_geometry_finish(const Translate& tr, int 
 template <int NT, bool CACHED>
 __device__ __forceinline__ void translate_rounds(const Translate& tr, const RowGeom& g, int r, int m,
                                                  const int32_t* chosen, const int32_t* cached, int ncached) {
-  constexpr int E = 8;
+  // Entries per lane per round.  4 against 8: the long-row selection 14.8 ->
+  // 14.5 us, the prefill selection 133-138 -> 132-133 us (back-to-back
+  // events, same box; 2 per lane measured between the two).  Less unrolled
+  // code, which runs once per row and cold.
+  constexpr int E = 4;
   const int c = tr.c, sh = c == 4 ? 2 : 0;
   const int nblk = c * m, total = nblk + g.p;
   const int32_t* pt = tr.page_table + (int64_t)g.b * tr.pt_stride;
