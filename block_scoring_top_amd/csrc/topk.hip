@@ -18,12 +18,14 @@
 // CDNA4 has no thread-block clusters or distributed shared memory.  The
 // blog's paths become:
 //   * rows shorter than 32,769 entries: one workgroup per row, the row held
-//     in registers, 1,024 lanes x 16 values (longer rows streamed twice), or
-//     512 lanes x 64 values for rows of up to 32,768 entries, or, for batches
-//     of at least 1,024 rows of at most 16,384 entries, 256 lanes x 64 values
-//     so that several rows share a CU.  The register path keeps each entry's
-//     bin, not its value, and marks the entries above and in the boundary bin
-//     with two bit masks;
+//     in registers: 512 lanes x 4 values for rows of up to 2,048 entries in
+//     small batches, 1,024 lanes x 16 values (longer rows streamed twice),
+//     512 lanes x 64 values for rows of up to 32,768 entries (read 16 bytes
+//     per lane when the rows start aligned), or, for batches of at least
+//     1,024 rows of at most 16,384 entries, 256 lanes x 64 values so that
+//     several rows share a CU.  The register path keeps each entry's bin, not
+//     its value, and marks the entries above and in the boundary bin with two
+//     bit masks;
 //   * long rows (>= 32,769 entries, any number of rows): one launch, one
 //     512-lane workgroup per 8,192-entry chunk, the chunk in registers (the
 //     launch's rows shorter than that are each selected whole by their first
