@@ -44,6 +44,7 @@ SEEDS = {
     "qsa_compress_prefill_8k": 1007,
     "qsa_compress_decode_64req": 1008,
     "select_mixed_300rows": 1009,
+    "topk_1x1m": 1010,
 }
 
 # Rotary parameters of the compressed index key.  The pages name an MRoPE
@@ -348,6 +349,13 @@ def topk_8x80k(seed: int = SEEDS["topk_8x80k"], rows: int = 8, n: int = 81920,
                      row_len=np.full(rows, n, dtype=np.int32), seed=seed)
 
 
+def topk_1x1m(seed: int = SEEDS["topk_1x1m"], rows: int = 1, n: int = 1_000_000, k: int = 2048) -> ScoreRows:
+    """Top-k only on one row of a million entries (the pages' 1M-token ISL
+    case of TopK-V2), with the value recipe of topk_8x80k."""
+    w = topk_8x80k(seed=seed, rows=rows, n=n, k=k)
+    return ScoreRows(name="topk_1x1m", k=k, scores=w.scores, row_len=w.row_len, seed=seed)
+
+
 def verify_lengths(rng: np.random.Generator, B: int, lo: int = 4096, hi: int = 131072):
     """Context lengths log-uniform in [lo, hi], rounded to a multiple of 4,
     and 0-3 pending tokens per request."""
@@ -469,6 +477,7 @@ WORKLOADS = {
     "qsa_compress_prefill_8k": qsa_compress_prefill_8k,
     "qsa_compress_decode_64req": qsa_compress_decode_64req,
     "select_mixed_300rows": select_mixed_300rows,
+    "topk_1x1m": topk_1x1m,
 }
 
 

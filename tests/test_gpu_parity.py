@@ -192,6 +192,14 @@ def test_topk_cfg_8x80k_exact():
     check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
 
 
+def test_topk_1x1m_exact():
+    # The one-million-entry row that bench.py times (123 chunks, one launch).
+    w = synth.topk_1x1m()
+    (out,), _ = gu.gpu_topk(w.scores, w.row_len, w.k)
+    ref_sel, ref_cnt = oracle.topk(w.scores, w.row_len, w.k)
+    check_topk_exact(out[0], out[1], ref_sel, ref_cnt)
+
+
 @pytest.mark.parametrize("n", [1, 7, 511, 512, 513, 2047, 2048, 2049, 4096, 16383, 16384, 16385, 32768, 32769,
                                50000])
 def test_topk_lengths_and_tie_storms(n):
