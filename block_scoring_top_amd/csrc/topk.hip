@@ -1094,12 +1094,6 @@ __device__ __forceinline__ uint32_t ws_buffer_load32(__amdgpu_buffer_rsrc_t rs, 
   constexpr int kSc1 = 16;
   return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kSc1);
 }
-__device__ __forceinline__ uint32_t ws_load32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ws_load64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Rows of >= kLongMin entries: one workgroup per CH = NT*16-entry chunk
 // (grid y); shorter rows are selected whole by their first workgroup.
