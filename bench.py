@@ -318,7 +318,7 @@ def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
               "timed region")
     if scorer == "decode":
         # More than two rows per request (rounded up) go to the matrix-core
-        # rows kernel; the traffic record holds the VALU kernel only.
+        # rows kernel (its own trace and traffic records).
         mfma_rows = -(-inp.num_rows // inp.num_req) > 2
         kname = "score_rows_mfma_kernel" if mfma_rows else "score_decode_kernel"
         dig = source_digest("score_decode.hip", "device.h")
@@ -327,7 +327,7 @@ def run_workload(name, K, warmup, dev, fused=True, cold_reps=False):
         tr = kernel_trace_us(f"{name}:{kname}", dig)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": None if mfma_rows else measured_traffic("score_decode", dig, name),
+                "traffic": measured_traffic("score_rows_mfma" if mfma_rows else "score_decode", dig, name),
                 "kernel": kname, "algorithmic_bytes": alg, "avg_us": round(t_score * 1e3, 2), "avg_us_method": method,
                 "avg_us_in_steps": round(kt["in_steps_ms"] * 1e3, 2),
                 "kernel_trace_avg_us": tr,
