@@ -873,19 +873,22 @@ def test_planned_plan_reused_across_k():
     assert cut == 16385  # 12 rows fit on the device at once, so rows from 16,385 entries on are split
 
 
-def test_planned_many_rows_keep_medium_rows_whole():
+@pytest.mark.parametrize("extra_ld", [0, 1])
+def test_planned_many_rows_keep_medium_rows_whole(extra_ld):
     # More items at the low split length than the device holds at once: the
     # plan splits only rows of 32,769 entries or more, and the 16,385-32,768
-    # rows are selected whole (streamed).
+    # rows are selected whole (512 lanes x 64 entries); at an aligned and at
+    # an odd row stride.
     rng = np.random.default_rng(1800)
     R, c, k = 1100, 1, 2048
     lens = rng.integers(16385, 32769, R).astype(np.int32)
     lens[:4] = [16385, 24576, 32768, 2]
     lens[4:8] = [32769, 40000, 65536, 49152]
+    lens[16:20] = [16386, 16387, 32767, 30001]  # ends inside a 16-byte quad
     ctx = [int(c * (n + 1)) for n in lens]
     inp = _given_rows_batch(rng, ctx, c, k)
-    rows = rng.standard_normal((R, 65536)).astype(np.float32)
-    rows[8:16] = synth.tie_storm_rows(1801, 8, 65536)
+    rows = rng.standard_normal((R, 65536 + extra_ld)).astype(np.float32)
+    rows[8:16, :65536] = synth.tie_storm_rows(1801, 8, 65536)
     header, outs = _planned_given(inp, rows, lens, 65536, reps=1)
     assert _check_planned(rows, lens, 65536, header, outs) == 32769
 
