@@ -1105,8 +1105,9 @@ __device__ __forceinline__ uint32_t ws_buffer_load32(__amdgpu_buffer_rsrc_t rs, 
 // the floor is a candidate.  If those would not fit in the chunk's slots, the
 // floor moves one bin up (fewer than q candidates); if the chunk keeps every
 // entry, its floor is 0.  It publishes its histogram at and above the floor,
-// its candidates (staged in LDS, stored coalesced) and (count, floor), waits
-// for those stores and arrives on the row's counter.
+// its candidates (written straight to its slots, positions handed out by one
+// LDS reservation per wave) and (count, floor), waits for those stores and
+// arrives on the row's counter.
 //
 // Resolution, by the last chunk to arrive.  Let U be the union of the
 // candidates and T the threshold bin of U for k (from the sum of the
@@ -1116,11 +1117,12 @@ __device__ __forceinline__ uint32_t ws_buffer_load32(__amdgpu_buffer_rsrc_t rs, 
 // above-threshold entries and its boundary bin are U's, and selecting within
 // U is exact.  Otherwise (a chunk holding more of the row's top than its
 // quota) the workgroup selects the whole row itself, streaming it.  The
-// candidates are read back in one round trip (every chunk's slot range,
-// validated against the published counts), emitted above T (count, block
-// scan, LDS) and refined in bin T on the composite (FP32 key, inverted
-// index); then the selection is written out and translated, and the row's
-// arrival counter is reset for the next call.
+// candidates are read back in one round trip (every chunk's slot range;
+// unused slots carry a marker), emitted above T (one packed LDS reservation
+// per wave) and refined in bin T on the composite (FP32 key, inverted
+// index); then the selection is written out and translated, and the first
+// word of each 64 KiB block of the row's record (its arrival counter among
+// them) is left zero for the next call.
 // One work item of the long-row selection: chunk w of row r, for a row of at
 // least `cut` entries.  Without KNOWN_N the length is read from row_len while
 // the chunk's score loads are in flight, and a shorter row is selected whole
