@@ -93,3 +93,44 @@ def test_random_batch_exact(shape, i):
                                      o[2], o[4], plan, out_pos=o[3], workspace=pws)
     torch.cuda.synchronize()
     check(o)
+
+
+SCORER_CASES = [(scorer, i) for scorer in ("decode", "prefill") for i in range(6)]
+
+
+@pytest.mark.parametrize("scorer,i", SCORER_CASES)
+def test_random_indexer_batch(scorer, i):
+    # Score -> select+translate on a random paged batch: 1-16 requests with
+    # log-uniform contexts; decode rows at arbitrary positions of their
+    # request (1-8 per request, unsorted, repeats allowed), prefill rows a
+    # consecutive chunk ending at the context's end.  Scores within the
+    # tolerance, top-k of the GPU's scores exact, end-to-end selection inside
+    # the tie band, expansion exact.
+    import gpu_util as gu
+    from checkers import check_scores, check_topk_e2e
+    rng = np.random.default_rng(5000 + 11 * i + (0 if scorer == "decode" else 500))
+    c = int(rng.choice([1, 4]))
+    k = int(rng.choice([16, 512, 2048]))
+    B = int(rng.integers(1, 17))
+    hi = 40000 if c == 4 else 12000
+    ctx = [int(np.exp(rng.uniform(0.0, np.log(hi)))) + 1 for _ in range(B)]
+    if scorer == "decode":
+        rows = [sorted(rng.integers(0, t, int(rng.integers(1, 9))).tolist(), key=lambda _: rng.random())
+                for t in ctx]
+    else:
+        rows = []
+        for t in ctx:
+            m = int(rng.integers(1, min(t, 200) + 1))
+            rows.append(list(range(t - m, t)))
+    inp = synth.build_paged_batch(f"random_{scorer}", 0, c=c, k=k, ctx_tokens=ctx, row_pos_per_req=rows, rng=rng)
+    say(f"random indexer case {scorer}/{i}: requests={B} rows={inp.num_rows} max_vis={inp.max_vis} c={c} k={k}")
+    g = gu.run_path(inp, scorer, True, False)
+    ref = oracle.pipeline(inp)
+    assert np.array_equal(g["row_len"], ref["row_len"])
+    check_scores(g["scores"], ref["scores"], ref["row_len"])
+    ld = max(inp.max_vis, 1)
+    s_gpu, c_gpu = oracle.topk(np.ascontiguousarray(g["scores"][:, :ld]), g["row_len"], inp.k)
+    check_topk_exact(g["sel"], g["sel_count"], s_gpu, c_gpu)
+    check_topk_e2e(g["sel"], g["sel_count"], ref["scores"], ref["sel"], ref["sel_count"], ref["row_len"])
+    rs, rp, rc = oracle.expand_translate(inp, g["sel"], g["sel_count"])
+    check_expand_exact(g["slots"], g["pos"], g["out_count"], rs, rp, rc, pending_counts(inp))
